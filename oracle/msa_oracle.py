@@ -1,0 +1,420 @@
+"""fp64 CPU oracle for MSA main attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product path (the HIP library and
+its Python binding) never calls it and shares no code with it.
+
+What it computes (sources are the four NeMo AutoModel API pages on the
+MiniMax-M3 MSA kernels):
+
+* Attention (msa_backward_sm100 page, module description and ``run_backward``;
+  msa_schedule page, ``QUERY_CHUNK`` and ``SOFTMAX_SCALE``).  Query head h of
+  a document belongs to index/KV head i = h // 16.  A query at
+  document-local position p lies in chunk c = p // 8 and sees the keys
+        A(p) = { j : j <= p, j < len_d, j // B in Sel[i, c] }.
+  With s_j = scale * q_p . k_j it outputs LSE_p = ln sum_{j in A} exp(s_j),
+  P_pj = exp(s_j - LSE_p) and O_p = sum_j P_pj v_j.  The backward takes dO
+  and returns dV_j = sum_{p,h} P_pj dO_p, dK_j = scale sum_{p,h} dS_pj q_p,
+  dQ_p = scale sum_j dS_pj k_j with dS_pj = P_pj (dO_p . v_j - D_p) and
+  D_p = dO_p . O_p (the backward preprocess, kernels page submodule list).
+  This is the exact result the method reaches; only the summation order of
+  an implementation differs.
+* Selection semantics: Sel[i, c] is a *set* of document-local block ids.
+  Slots holding -1 are empty; ids outside the document, ids of blocks that
+  start after the chunk's last query, and repeated ids add no key to A(p),
+  so they are dropped and counted (``clean_selection``).
+* k2q CSR (msa_schedule page, ``MSABackwardSchedule.row_ptr`` and
+  ``q_indices``): per index head one CSR row per key block, rows ordered by
+  (document, block); the entries of a row are the document-local first query
+  positions (8 c) of the chunks that selected the block, ascending.
+* Walk rule and task table (msa_schedule page, ``rows_per_cta``,
+  ``chunk_map``, ``grid_launch_bound``, ``ROWS_PER_CTA_*``, and the
+  ``scheduler_metadata`` column order).
+
+Floating point is fp64 throughout; bf16 inputs are widened exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# msa_schedule page, module data.
+QUERY_CHUNK = 8
+ROWS_PER_CTA_SMALL = 4
+ROWS_PER_CTA_LARGE = 64
+ROWS_PER_CTA_SWITCH = 2400
+Q_HEADS_PER_INDEX = 16          # msa_backward_sm100 page, MAIN_HEADS_PER_INDEX = 64 // 4
+TASK_COLUMNS = ("index_head", "row_linear", "q_begin", "q_count",
+                "document_ordinal", "document_local_kblock")
+
+
+def f64(x) -> np.ndarray:
+    """Widen a bf16/fp32 torch tensor or array to fp64 numpy (exact)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+class DocLayout:
+    """Document geometry from cu_seqlens (msa_schedule page, ``cu_seqlens``)."""
+
+    def __init__(self, cu_seqlens, block: int, chunk: int = QUERY_CHUNK):
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        self.cu = cu
+        self.lens = np.diff(cu)
+        self.docs = len(self.lens)
+        self.block = int(block)
+        self.chunk = int(chunk)
+        self.nchunks = -(-self.lens // self.chunk)
+        self.nblocks = -(-self.lens // self.block)
+        self.chunk_off = np.concatenate([[0], np.cumsum(self.nchunks)]).astype(np.int64)
+        self.blk_off = np.concatenate([[0], np.cumsum(self.nblocks)]).astype(np.int64)
+        self.C = int(self.chunk_off[-1])
+        self.R = int(self.blk_off[-1])
+        # document of every global chunk / every global key-block row
+        self.chunk_doc = np.repeat(np.arange(self.docs), self.nchunks)
+        self.row_doc = np.repeat(np.arange(self.docs), self.nblocks)
+
+    def chunk_local(self, g: int) -> tuple[int, int]:
+        d = int(self.chunk_doc[g])
+        return d, int(g - self.chunk_off[d])
+
+
+# ---------------------------------------------------------------------------
+# Selection, CSR, walk, tasks
+# ---------------------------------------------------------------------------
+
+def clean_selection(sel: np.ndarray, layout: DocLayout) -> tuple[np.ndarray, int]:
+    """Keep each id that adds keys to A(p), once, in its slot; -1 elsewhere.
+
+    Returns (sel_clean [Hkv, C, k] int32, number of dropped non-empty slots).
+    An id b is kept for chunk c of document d when 0 <= b < ceil(len_d / B),
+    b * B <= the chunk's last query position, and no earlier slot of the same
+    chunk kept b.
+    """
+    sel = np.asarray(sel, dtype=np.int64)
+    hkv, C, k = sel.shape
+    assert C == layout.C
+    d = layout.chunk_doc
+    c_local = np.arange(C) - layout.chunk_off[d]
+    last_q = np.minimum(c_local * layout.chunk + layout.chunk - 1, layout.lens[d] - 1)
+    nb = layout.nblocks[d]
+    valid = (sel >= 0) & (sel < nb[None, :, None]) & (sel * layout.block <= last_q[None, :, None])
+    out = np.where(valid, sel, -1)
+    for s in range(1, k):              # drop repeats of an id kept in an earlier slot
+        dup = np.zeros((hkv, C), dtype=bool)
+        for s2 in range(s):
+            dup |= (out[:, :, s2] == out[:, :, s]) & (out[:, :, s] >= 0)
+        out[:, :, s] = np.where(dup, -1, out[:, :, s])
+    dropped = int(np.count_nonzero((sel != -1) & (out == -1)))
+    return out.astype(np.int32), dropped
+
+
+def build_k2q_csr(sel_clean: np.ndarray, layout: DocLayout):
+    """Invert the per-chunk selection into key-block -> query buckets.
+
+    Returns (row_ptr [Hkv, R+1] int32, q_idx [Hkv, C*k] int32, padded with -1).
+    Row r = blk_off[d] + b; entries are 8*c (document-local chunk start),
+    ascending within a row.  A stable sort by (row, chunk) is the only step.
+    """
+    hkv, C, k = sel_clean.shape
+    R = layout.R
+    row_ptr = np.zeros((hkv, R + 1), dtype=np.int32)
+    q_idx = np.full((hkv, C * k), -1, dtype=np.int32)
+    d = layout.chunk_doc
+    c_local = np.arange(C) - layout.chunk_off[d]
+    for i in range(hkv):
+        g, s = np.nonzero(sel_clean[i] >= 0)
+        rows = layout.blk_off[d[g]] + sel_clean[i, g, s]
+        order = np.lexsort((g, rows))          # by row, then by chunk
+        counts = np.bincount(rows, minlength=R)
+        row_ptr[i, 1:] = np.cumsum(counts)
+        q_idx[i, : len(order)] = (c_local[g] * layout.chunk)[order]
+    return row_ptr, q_idx
+
+
+def rows_per_cta(num_rows: int) -> int:
+    """Walk length (msa_schedule page, ``rows_per_cta``): the small walk below
+    ROWS_PER_CTA_SWITCH rows, the large one from there on."""
+    return ROWS_PER_CTA_SMALL if num_rows < ROWS_PER_CTA_SWITCH else ROWS_PER_CTA_LARGE
+
+
+def chunk_map(num_rows: int, rpc: int, num_sms: int) -> tuple[int, int, int]:
+    """(num_full_ctas, tail_rows, grid_ctas) (msa_schedule page, ``chunk_map``).
+
+    Full walks take ``rpc`` rows each; the tail rows left over are spread over
+    at most one extra walk per SM (min(tail_rows, num_sms) walks), so that
+    grid_ctas <= num_rows // rpc + num_sms as the page states.
+    """
+    full = num_rows // rpc
+    tail = num_rows - full * rpc
+    return full, tail, full + min(tail, num_sms)
+
+
+def walk_bounds(num_rows: int, rpc: int, num_sms: int, cta: int) -> tuple[int, int]:
+    """Rows [lo, hi) walked by workgroup ``cta``: full walks first, then the
+    tail split as evenly as possible, earlier tail walks taking one more row."""
+    full, tail, grid = chunk_map(num_rows, rpc, num_sms)
+    if cta < full:
+        return cta * rpc, (cta + 1) * rpc
+    t = cta - full
+    nt = grid - full
+    assert 0 <= t < nt
+    base, extra = divmod(tail, nt)
+    lo = full * rpc + t * base + min(t, extra)
+    return lo, lo + base + (1 if t < extra else 0)
+
+
+def grid_launch_bound(capacity: int, num_sms: int) -> int:
+    """Grid size that covers every count in [0, capacity] (msa_schedule page,
+    ``grid_launch_bound``): full walks plus at most one tail walk per SM, the
+    larger of the small-walk and the large-walk regime."""
+    small = min(capacity, ROWS_PER_CTA_SWITCH - 1) // ROWS_PER_CTA_SMALL
+    large = capacity // ROWS_PER_CTA_LARGE if capacity >= ROWS_PER_CTA_SWITCH else 0
+    return max(small, large) + num_sms
+
+
+def build_tasks(row_ptr: np.ndarray, q_idx: np.ndarray, layout: DocLayout, num_sms: int):
+    """Task table in CSR order, heads first (msa_schedule page,
+    ``scheduler_metadata`` columns), and the walk descriptor.
+
+    Returns (task_meta [Hkv*C*k, 6] int32 padded with -1, desc int32 [8]) with
+    desc = (N, rows_per_cta, num_full, tail_rows, tail_ctas, grid_ctas, capacity, 0).
+    """
+    hkv = row_ptr.shape[0]
+    cap = q_idx.shape[1] * hkv
+    meta = np.full((cap, 6), -1, dtype=np.int32)
+    t = 0
+    for i in range(hkv):
+        n_i = int(row_ptr[i, -1])
+        counts = np.diff(row_ptr[i].astype(np.int64))
+        rows = np.repeat(np.arange(layout.R), counts)
+        docs = layout.row_doc[rows]
+        qb = q_idx[i, :n_i].astype(np.int64)
+        meta[t:t + n_i, 0] = i
+        meta[t:t + n_i, 1] = rows
+        meta[t:t + n_i, 2] = qb
+        meta[t:t + n_i, 3] = np.minimum(layout.chunk, layout.lens[docs] - qb)
+        meta[t:t + n_i, 4] = docs
+        meta[t:t + n_i, 5] = rows - layout.blk_off[docs]
+        t += n_i
+    n = t
+    rpc = rows_per_cta(n)
+    full, tail, grid = chunk_map(n, rpc, num_sms)
+    desc = np.array([n, rpc, full, tail, grid - full, grid, cap, 0], dtype=np.int32)
+    return meta, desc
+
+
+def build_schedule(sel: np.ndarray, cu_seqlens, block: int, num_sms: int):
+    """Everything the schedule build produces, as a dict of int arrays."""
+    layout = DocLayout(cu_seqlens, block)
+    sel_clean, dropped = clean_selection(sel, layout)
+    row_ptr, q_idx = build_k2q_csr(sel_clean, layout)
+    meta, desc = build_tasks(row_ptr, q_idx, layout, num_sms)
+    return dict(layout=layout, sel_clean=sel_clean, dropped=dropped, row_ptr=row_ptr,
+                q_idx=q_idx, task_meta=meta, desc=desc)
+
+
+# ---------------------------------------------------------------------------
+# Attention, literal dense mode (T x T masks per document and head)
+# ---------------------------------------------------------------------------
+
+def visibility_mask(layout: DocLayout, sel_clean: np.ndarray, i: int, d: int) -> np.ndarray:
+    """M[p, j] = (j <= p) and (j // B in Sel[i, p // 8]) for one document."""
+    n = int(layout.lens[d])
+    chosen = np.zeros((int(layout.nchunks[d]), max(int(layout.nblocks[d]), 1)), dtype=bool)
+    g0 = int(layout.chunk_off[d])
+    for c in range(int(layout.nchunks[d])):
+        for b in sel_clean[i, g0 + c]:
+            if b >= 0:
+                chosen[c, b] = True
+    p = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= p) & chosen[p // layout.chunk, j // layout.block]
+
+
+def forward_dense(q, k, v, cu_seqlens, sel_clean, block: int, scale: float):
+    """O [T, Hq, D] and LSE [T, Hq] (natural log; -inf and O = 0 for an empty A(p))."""
+    q, k, v = f64(q), f64(k), f64(v)
+    layout = DocLayout(cu_seqlens, block)
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    out = np.zeros_like(q)
+    lse = np.full((T, Hq), -np.inf)
+    for d in range(layout.docs):
+        a, b_ = int(layout.cu[d]), int(layout.cu[d + 1])
+        if b_ == a:
+            continue
+        for i in range(k.shape[1]):
+            M = visibility_mask(layout, sel_clean, i, d)
+            any_row = M.any(axis=1)
+            K, V = k[a:b_, i], v[a:b_, i]
+            for h in range(G * i, G * (i + 1)):
+                S = scale * (q[a:b_, h] @ K.T)
+                S = np.where(M, S, -np.inf)
+                m = np.where(any_row, S.max(axis=1), 0.0)
+                with np.errstate(divide="ignore"):
+                    l_ = np.log(np.exp(S - m[:, None]).sum(axis=1)) + m
+                l_ = np.where(any_row, l_, -np.inf)
+                P = np.where(M, np.exp(S - np.where(any_row, l_, 0.0)[:, None]), 0.0)
+                out[a:b_, h] = P @ V
+                lse[a:b_, h] = l_
+    return out, lse
+
+
+def backward_dense(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: float):
+    """(dq, dk, dv, delta, out, lse) by the analytic backward, dense masks."""
+    q, k, v, do = f64(q), f64(k), f64(v), f64(do)
+    out, lse = forward_dense(q, k, v, cu_seqlens, sel_clean, block, scale)
+    layout = DocLayout(cu_seqlens, block)
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    delta = (do * out).sum(axis=-1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for d in range(layout.docs):
+        a, b_ = int(layout.cu[d]), int(layout.cu[d + 1])
+        if b_ == a:
+            continue
+        for i in range(k.shape[1]):
+            M = visibility_mask(layout, sel_clean, i, d)
+            K, V = k[a:b_, i], v[a:b_, i]
+            for h in range(G * i, G * (i + 1)):
+                S = scale * (q[a:b_, h] @ K.T)
+                L = lse[a:b_, h]
+                P = np.where(M, np.exp(S - np.where(np.isfinite(L), L, 0.0)[:, None]), 0.0)
+                dP = do[a:b_, h] @ V.T
+                dS = P * (dP - delta[a:b_, h][:, None])
+                dq[a:b_, h] = scale * (dS @ K)
+                dk[a:b_, i] += scale * (dS.T @ q[a:b_, h])
+                dv[a:b_, i] += P.T @ do[a:b_, h]
+    return dq, dk, dv, delta, out, lse
+
+
+# ---------------------------------------------------------------------------
+# Attention, block-gathered mode (only the selected keys of each chunk)
+# ---------------------------------------------------------------------------
+
+def chunk_keys(layout: DocLayout, sel_clean: np.ndarray, i: int, g: int):
+    """(doc, doc-local query positions, doc-local key positions) of chunk g."""
+    d, c = layout.chunk_local(g)
+    n = int(layout.lens[d])
+    blocks = sorted({int(b) for b in sel_clean[i, g] if b >= 0})
+    keys = [np.arange(b * layout.block, min((b + 1) * layout.block, n)) for b in blocks]
+    keys = np.concatenate(keys) if keys else np.zeros(0, dtype=np.int64)
+    qpos = np.arange(c * layout.chunk, min((c + 1) * layout.chunk, n))
+    return d, qpos, keys
+
+
+def _take(x, tokens, heads) -> np.ndarray:
+    """x[tokens][:, heads] as fp64 numpy, for numpy arrays or torch tensors."""
+    if isinstance(x, np.ndarray):
+        return np.asarray(x[np.asarray(tokens)][:, np.asarray(heads)], dtype=np.float64)
+    import torch
+    t = torch.as_tensor(np.asarray(tokens, dtype=np.int64))
+    h = torch.as_tensor(np.asarray(heads, dtype=np.int64))
+    return f64(x.index_select(0, t).index_select(1, h))
+
+
+def _chunk_probs(qh, K, qpos, keys, scale):
+    """S [nq, G, nk] -> (P, LSE) for one chunk and one head group."""
+    nq, G, D = qh.shape
+    S = scale * (qh.reshape(nq * G, D) @ K.T).reshape(nq, G, -1)
+    M = (keys[None, :] <= qpos[:, None])[:, None, :]
+    S = np.where(M, S, -np.inf)
+    any_row = M.any(axis=2)
+    m = np.where(any_row, S.max(axis=2, initial=-np.inf), 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.log(np.exp(S - m[..., None]).sum(axis=2)) + m
+    lse = np.where(any_row, lse, -np.inf)
+    P = np.where(M, np.exp(S - np.where(any_row, lse, 0.0)[..., None]), 0.0)
+    return P, lse
+
+
+def forward_chunk(q, k, v, layout, sel_clean, i, g, scale):
+    """Oracle rows of one (index head, chunk): (tokens, heads, O, LSE)."""
+    d, qpos, keys = chunk_keys(layout, sel_clean, i, g)
+    G = q.shape[1] // k.shape[1]
+    tq = int(layout.cu[d]) + qpos
+    tk = int(layout.cu[d]) + keys
+    heads = np.arange(G * i, G * (i + 1))
+    qh = _take(q, tq, heads)
+    K = _take(k, tk, [i])[:, 0]
+    V = _take(v, tk, [i])[:, 0]
+    P, lse = _chunk_probs(qh, K, qpos, keys, scale)
+    nq = len(qpos)
+    O = (P.reshape(nq * G, -1) @ V).reshape(nq, G, -1)
+    return tq, heads, O, lse
+
+
+def forward_gathered(q, k, v, cu_seqlens, sel_clean, block: int, scale: float,
+                     chunks=None):
+    """O and LSE over the selected keys only; ``chunks`` = iterable of (i, g)
+    restricts the work (rows outside stay O = 0, LSE = nan)."""
+    q, k, v = f64(q), f64(k), f64(v)
+    layout = DocLayout(cu_seqlens, block)
+    T, Hq, D = q.shape
+    out = np.zeros_like(q)
+    lse = np.full((T, Hq), np.nan)
+    if chunks is None:
+        chunks = [(i, g) for i in range(k.shape[1]) for g in range(layout.C)]
+    for i, g in chunks:
+        tq, heads, O, L = forward_chunk(q, k, v, layout, sel_clean, i, g, scale)
+        out[np.ix_(tq, heads)] = O
+        lse[np.ix_(tq, heads)] = L
+    return out, lse
+
+
+def backward_gathered(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: float,
+                      chunks=None):
+    """(dq, dk, dv, delta, out, lse) over the selected keys only.  With
+    ``chunks`` given, only those (i, g) contribute: dq rows of those chunks
+    are complete, and dk/dv rows are complete for key blocks whose every
+    selecting chunk is listed."""
+    q, k, v, do = f64(q), f64(k), f64(v), f64(do)
+    layout = DocLayout(cu_seqlens, block)
+    T, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    out = np.zeros_like(q)
+    lse = np.full((T, Hq), np.nan)
+    delta = np.full((T, Hq), np.nan)
+    if chunks is None:
+        chunks = [(i, g) for i in range(k.shape[1]) for g in range(layout.C)]
+    for i, g in chunks:
+        d, qpos, keys = chunk_keys(layout, sel_clean, i, g)
+        tq = int(layout.cu[d]) + qpos
+        tk = int(layout.cu[d]) + keys
+        heads = np.arange(G * i, G * (i + 1))
+        qh, doh = q[tq][:, heads], do[tq][:, heads]
+        K, V = k[tk, i], v[tk, i]
+        P, L = _chunk_probs(qh, K, qpos, keys, scale)
+        nq = len(qpos)
+        O = (P.reshape(nq * G, -1) @ V).reshape(nq, G, D)
+        Dl = (doh * O).sum(axis=-1)
+        dP = (doh.reshape(nq * G, D) @ V.T).reshape(nq, G, -1)
+        dS = P * (dP - Dl[..., None])
+        dq[np.ix_(tq, heads)] = scale * (dS.reshape(nq * G, -1) @ K).reshape(nq, G, D)
+        if len(tk):
+            dk[tk, i] += scale * (dS.reshape(nq * G, -1).T @ qh.reshape(nq * G, D))
+            dv[tk, i] += P.reshape(nq * G, -1).T @ doh.reshape(nq * G, D)
+        out[np.ix_(tq, heads)] = O
+        lse[np.ix_(tq, heads)] = L
+        delta[np.ix_(tq, heads)] = Dl
+    return dq, dk, dv, delta, out, lse
+
+
+def chunks_selecting_block(sched: dict, i: int, row: int) -> list[tuple[int, int]]:
+    """(i, g) of every chunk whose clean selection holds key-block row ``row``
+    (read from the oracle's own CSR)."""
+    layout = sched["layout"]
+    rp, qi = sched["row_ptr"][i], sched["q_idx"][i]
+    d = int(layout.row_doc[row])
+    return [(i, int(layout.chunk_off[d]) + int(x) // layout.chunk)
+            for x in qi[rp[row]:rp[row + 1]]]
