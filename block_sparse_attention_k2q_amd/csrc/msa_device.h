@@ -1,0 +1,108 @@
+// Device helpers shared by the gfx950 kernels of libmsa.
+//
+// MFMA and LDS-transpose lane layouts used below (CDNA4, wave64):
+//  v_mfma_f32_32x32x16_bf16  A (32 x 16): lane l holds row l%32, k = 8*(l/32) + 0..7
+//                            B (16 x 32): lane l holds col l%32, k = 8*(l/32) + 0..7
+//                            C (32 x 32): lane l, register j holds col l%32,
+//                                         row 8*(j/4) + 4*(l/32) + j%4
+//  ds_read_tr16_b64          in each 16-lane group g, lane 16g + x receives, as
+//                            element r (0..3), 16-bit element x%4 of the 8 bytes
+//                            addressed by lane 16g + 4r + x/4.
+// An accumulator can feed a later MFMA as an A or B operand directly when the
+// contraction runs over its row index: the row order inside a 16-wide k step
+// is a permutation, and the other operand is read in the same permuted order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 8;        // queries per chunk
+constexpr int kQPerKV = 16;      // query heads per index/KV head
+constexpr int kTileM = 128;      // 8 queries x 16 heads
+constexpr int kBlock = 64;       // key block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ floatx16 mfma32(const bf16x8& a, const bf16x8& b, const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One transposing LDS read of 4 bf16 (see the layout note above).
+__device__ __forceinline__ shortx4 lds_read_tr4(const void* lds_ptr) {
+  lds_shortx4* p = (lds_shortx4*)(const_cast<void*>(lds_ptr));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(shortx4 lo, shortx4 hi) {
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  shortx8 s = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, s);
+}
+
+// Operand for a K step of 16 along the rows of a row-major [rows][cols] bf16
+// tile in LDS (element (r, c) at base + r*ld + c): lane l receives column
+// col0 + l%32 and, as elements 0..7, rows
+//   row_lo(h) + 0..3 and row_hi(h) + 0..3, h = l/32,
+// where the caller passes row_lo/row_hi for its own h.  Used for operands
+// whose contraction index is the tile's row index.
+__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* base, int ld, int col0, int lane,
+                                                 int row_lo_h0, int row_lo_h1, int row_hi_h0,
+                                                 int row_hi_h1) {
+  // Source-lane role: this lane supplies the address for group g = lane/16,
+  // row r = (lane%16)/4, 4-column chunk c = lane%4.
+  const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+  const int h = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * c;
+  const int rlo = (h ? row_lo_h1 : row_lo_h0) + r;
+  const int rhi = (h ? row_hi_h1 : row_hi_h0) + r;
+  shortx4 lo = lds_read_tr4(base + rlo * ld + col);
+  shortx4 hi = lds_read_tr4(base + rhi * ld + col);
+  return join_tr(lo, hi);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store_bf16x8(bf16* p, bf16x8 v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+__device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Value held by lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// Index of the last element <= x in a non-decreasing array a[0..n) (a[0] <= x).
+__device__ __forceinline__ int upper_bound_minus1(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace msa

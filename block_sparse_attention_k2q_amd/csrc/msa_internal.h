@@ -1,0 +1,78 @@
+// Host-side internals of libmsa: workspace layout and kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa.h"
+
+namespace msa {
+
+// Walk rule constants (msa_schedule page: ROWS_PER_CTA_SMALL / _LARGE / _SWITCH).
+constexpr int kRowsPerWalkSmall = 4;
+constexpr int kRowsPerWalkLarge = 64;
+constexpr int kRowsPerWalkSwitch = 2400;
+
+inline int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
+
+// Offsets (int32 elements) of the schedule workspace tables; see msa.h.
+inline msa_schedule_layout schedule_layout(const msa_problem& p) {
+  const int64_t hkv = p.num_kv_heads, C = p.num_chunks, K = p.topk, R = p.num_kblocks;
+  const int64_t cap = hkv * C * K;
+  msa_schedule_layout L;
+  int64_t o = 0;
+  L.desc = o; o += 8;
+  L.err = o; o += 8;
+  o = align64(o);
+  L.doc_chunk_off = o; o = align64(o + p.num_docs + 1);
+  L.doc_blk_off = o; o = align64(o + p.num_docs + 1);
+  L.chunk_doc = o; o = align64(o + C);
+  L.sel_clean = o; o = align64(o + cap);
+  L.row_cursor = o; o = align64(o + hkv * R);
+  L.row_ptr = o; o = align64(o + hkv * (R + 1));
+  L.head_off = o; o = align64(o + hkv + 1);
+  L.q_idx = o; o = align64(o + cap);
+  L.task_meta = o; o = align64(o + cap * 6);
+  L.total = o;
+  return L;
+}
+
+inline int64_t grid_launch_bound(int64_t cap, int num_cus) {
+  const int64_t small = (cap < kRowsPerWalkSwitch - 1 ? cap : kRowsPerWalkSwitch - 1) / kRowsPerWalkSmall;
+  const int64_t large = cap >= kRowsPerWalkSwitch ? cap / kRowsPerWalkLarge : 0;
+  return (small > large ? small : large) + num_cus;
+}
+
+// Scratch layout of the backward (bytes, 256-aligned): Delta, dQ pool, dK, dV.
+struct BackwardScratch {
+  size_t delta, dq_pool, dk_acc, dv_acc, total;
+};
+inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
+  auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t T = (size_t)p.total_tokens, hq = (size_t)p.num_kv_heads * p.q_per_kv,
+               hkv = (size_t)p.num_kv_heads, D = (size_t)p.head_dim;
+  BackwardScratch s;
+  size_t o = 0;
+  s.delta = o; o = a256(o + 4 * T * hq);
+  s.dq_pool = o; o = a256(o + 4 * T * hq * D);
+  s.dk_acc = o; o = a256(o + 4 * T * hkv * D);
+  s.dv_acc = o; o = a256(o + 4 * T * hkv * D);
+  s.total = o;
+  return s;
+}
+
+hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const int32_t* sel,
+                                 int32_t* sched, const msa_schedule_layout& L, hipStream_t stream);
+hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, const void* v,
+                          const int32_t* cu, const int32_t* sched, const msa_schedule_layout& L,
+                          void* out, float* lse, hipStream_t stream);
+hipError_t launch_backward_preprocess(const msa_problem& p, const void* out, const void* dout,
+                                      void* scratch, hipStream_t stream);
+hipError_t launch_backward_main(const msa_problem& p, const void* q, const void* k, const void* v,
+                                const void* dout, const float* lse, const int32_t* cu,
+                                const int32_t* sched, const msa_schedule_layout& L, void* scratch,
+                                hipStream_t stream);
+hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
+                                       void* dv, hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,159 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MSA main-attention library, libmsa.so.
+ *
+ * MSA main attention (MiniMax M3): every 8-query chunk, under each index
+ * head, attends only to a selected set of key blocks, with causal and
+ * per-document (cu_seqlens) masks.  Sources: NeMo AutoModel API pages
+ * "msa_bindings" (MSAKernels: CSR builder, flat forward, local backward),
+ * "kernels" (submodules: backward preprocess, main backward, postprocess,
+ * task build), "msa_schedule" (MSABackwardSchedule, the walk rule and the
+ * topology constants) and "msa_backward_sm100" (module description and
+ * run_backward).
+ *
+ * Conventions shared by every call
+ *  - Ownership: the caller owns every buffer.  The library allocates no
+ *    device memory and never synchronises; each call only enqueues kernels
+ *    on the given HIP stream (NULL = the default stream) and returns.
+ *  - Pointers named "device" must be device pointers, 16-byte aligned.
+ *  - Layouts are THD, token-major and contiguous:
+ *      q, out, dout, dq : bf16 [T, Hq, D]      (Hq = 16 * Hkv)
+ *      k, v, dk, dv     : bf16 [T, Hkv, D]
+ *      lse              : fp32 [T, Hq]          (natural log)
+ *      cu_seqlens       : int32 [num_docs + 1]  (device; cu[0] = 0, non-decreasing)
+ *      sel              : int32 [Hkv, C, topk]  (device; document-local key-block
+ *                         ids per (index head, chunk); -1 = empty slot)
+ *    Query head h belongs to index/KV head h / 16.
+ *  - Selections are sets: ids outside the document, ids of blocks that start
+ *    after the chunk's last query, and repeated ids add no keys, so the
+ *    schedule build drops them and counts them in the schedule's error words.
+ *  - Return value: an msa_status.  Host-side checks happen before anything is
+ *    enqueued; MSA_ERR_HIP reports a failed launch.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID = 1,      /* NULL pointer or negative size */
+  MSA_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or a size the kernels are not built for */
+  MSA_ERR_SHAPE = 3,        /* sizes inconsistent with each other */
+  MSA_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
+  MSA_ERR_HIP = 5           /* a HIP runtime call or launch failed */
+} msa_status;
+
+/* Problem geometry; all fields are host integers.  num_chunks, num_kblocks
+ * and max_doc_chunks must agree with cu_seqlens (the schedule build checks
+ * this on the device and sets MSA_SCHED_ERR_GEOMETRY if they do not). */
+typedef struct msa_problem {
+  int32_t total_tokens;    /* T = cu_seqlens[num_docs] */
+  int32_t num_docs;        /* >= 1 */
+  int32_t num_kv_heads;    /* Hkv: index heads == KV heads (one index head per KV head) */
+  int32_t q_per_kv;        /* query heads per KV head; must be 16 (8 queries x 16 heads = 128-row tile) */
+  int32_t head_dim;        /* D: 64 or 128 */
+  int32_t block_size;      /* B: key block size; must be 64 */
+  int32_t query_chunk;     /* must be 8 (msa_schedule: QUERY_CHUNK) */
+  int32_t topk;            /* slots per (index head, chunk); 1..64 */
+  int32_t num_chunks;      /* C = sum_d ceil(len_d / 8) */
+  int32_t num_kblocks;     /* R = sum_d ceil(len_d / B) */
+  int32_t max_doc_chunks;  /* max_d ceil(len_d / 8); <= MSA_MAX_DOC_CHUNKS */
+  int32_t num_cus;         /* compute units the walk is sized for (msa_device_check) */
+  float softmax_scale;     /* usually head_dim ** -0.5 (msa_schedule: SOFTMAX_SCALE) */
+} msa_problem;
+
+#define MSA_MAX_DOC_CHUNKS (1 << 18) /* documents up to 2 Mi tokens (32 KiB LDS bitmap per bucket sort) */
+
+/* Layout of the int32 schedule workspace (offsets in int32 elements).
+ * msa_schedule: MSABackwardSchedule carries row_ptr, q_indices,
+ * scheduler_metadata, work_count and cu_seqlens; this workspace holds the
+ * same tables plus the cleaned selection the forward reads.
+ *   desc[8]     : work_count N, rows_per_cta, num_full_walks, tail_rows,
+ *                 tail_walks, grid_walks, capacity (Hkv*C*topk), 0
+ *   err[8]      : [0] dropped selection slots, [1] geometry mismatch flag
+ *   doc_chunk_off[num_docs+1], doc_blk_off[num_docs+1] : per-document offsets
+ *   chunk_doc[C]          : document of each global chunk
+ *   sel_clean[Hkv*C*topk] : kept ids in their slots, -1 elsewhere
+ *   row_cursor[Hkv*R]     : build scratch
+ *   row_ptr[Hkv*(R+1)]    : k2q CSR offsets, one CSR per index head
+ *   head_off[Hkv+1]       : first task row of each index head
+ *   q_idx[Hkv*C*topk]     : CSR entries = document-local first query (8*c) of
+ *                           each selecting chunk, ascending per row; -1 padding
+ *   task_meta[Hkv*C*topk*6] : one task (128-row tile) per CSR entry, heads in
+ *                           order: (index_head, row_linear, q_begin, q_count,
+ *                           document_ordinal, document_local_kblock); -1 padding */
+typedef struct msa_schedule_layout {
+  int64_t desc, err, doc_chunk_off, doc_blk_off, chunk_doc, sel_clean, row_cursor,
+      row_ptr, head_off, q_idx, task_meta, total;
+} msa_schedule_layout;
+
+#define MSA_SCHED_ERR_DROPPED 0
+#define MSA_SCHED_ERR_GEOMETRY 1
+
+/* Device gate (kernels page: require_sm100 / sm_count analog).  Returns
+ * MSA_OK and the compute-unit count when `device` is a gfx950 GPU,
+ * MSA_ERR_UNSUPPORTED otherwise.  Results are memoised per device. */
+int msa_device_check(int device, int32_t* num_cus);
+
+/* Offsets of every table in the schedule workspace, and its total size. */
+int msa_schedule_layout_of(const msa_problem* p, msa_schedule_layout* out);
+
+/* k2q CSR build + task build (msa_bindings: build_k2q_csr; kernels page:
+ * msa_task_build; msa_schedule: MSABackwardSchedule, rows_per_cta, chunk_map).
+ * Cleans the selection, inverts it into key-block buckets (row r =
+ * doc_blk_off[d] + b), sorts each bucket by chunk, and writes the task table
+ * and the walk descriptor.  Inputs: cu_seqlens, sel (device).  Output: sched
+ * (device, msa_schedule_layout_of(...).total int32 elements). */
+int msa_build_schedule(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
+                       int32_t* sched, void* stream);
+
+/* Sparse forward (msa_bindings: the flat forward sparse_atten_func; its
+ * outputs are the out/lse that run_backward consumes).  For every
+ * (chunk, index head): online softmax over the chunk's kept key blocks with
+ * the causal mask; writes out (bf16) and lse (fp32, natural log; -inf and
+ * out = 0 where a query sees no key).  `sched` must come from
+ * msa_build_schedule on the same cu_seqlens and selection. */
+int msa_forward(const msa_problem* p, const void* q, const void* k, const void* v,
+                const int32_t* cu_seqlens, const int32_t* sched, void* out, float* lse,
+                void* stream);
+
+/* Bytes of fp32 scratch msa_backward needs: Delta [T, Hq], the dQ pool
+ * [T, Hq, D] and dK, dV accumulators [T, Hkv, D]. */
+int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
+
+/* KV-parallel backward (msa_backward_sm100: run_backward): preprocess
+ * (Delta = rowsum(dout * out), zero the accumulators), main kernel (per walk
+ * of task rows: K/V resident per bucket, five bf16 MFMA contractions per
+ * 128-row tile, dK/dV flushed per bucket segment with fp32 atomics, dQ
+ * scattered with fp32 atomics into the pool), postprocess (cast to bf16).
+ * dk/dv rows that no query attends are exactly 0. */
+int msa_backward(const msa_problem* p, const void* q, const void* k, const void* v,
+                 const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
+                 const int32_t* sched, void* scratch, void* dq, void* dk, void* dv, void* stream);
+
+/* The three steps of msa_backward, callable one at a time (same arguments
+ * and scratch; used to time each kernel).  Must run in this order. */
+int msa_backward_preprocess(const msa_problem* p, const void* out, const void* dout,
+                            void* scratch, void* stream);
+int msa_backward_main(const msa_problem* p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse, const int32_t* cu_seqlens,
+                      const int32_t* sched, void* scratch, void* stream);
+int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk,
+                             void* dv, void* stream);
+
+/* Grid size the main backward kernel is launched with (msa_schedule:
+ * grid_launch_bound(capacity, num_cus), capacity = Hkv * C * topk). */
+int64_t msa_grid_launch_bound(int64_t capacity, int32_t num_cus);
+
+const char* msa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,78 @@
+"""Host-side checks of the C-ABI library (no GPU needed): the library loads,
+exports every entry point include/msa.h declares, rejects bad problems before
+touching the device, and the binding fails loudly when the library is absent."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_k2q_amd import binding as B
+from oracle import msa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "msa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(msa_\w+)\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    h = B.lib()
+    for n in names:
+        assert hasattr(h, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_grid_launch_bound_matches_walk_rule():
+    for cap in (0, 1, 7, 2399, 2400, 61696, 65536, 1 << 20):
+        for s in (1, 7, 256):
+            assert B.msa_grid_launch_bound(cap, s) == O.grid_launch_bound(cap, s)
+
+
+def test_schedule_layout_is_host_only_and_sized():
+    p = B.Problem.make([0, 8192], 4, 128, 16)
+    L = B.msa_schedule_layout_of(p)
+    cap = 4 * 1024 * 16
+    assert L.task_meta + 6 * cap <= L.total
+    offs = [L.desc, L.err, L.doc_chunk_off, L.doc_blk_off, L.chunk_doc, L.sel_clean, L.row_cursor,
+            L.row_ptr, L.head_off, L.q_idx, L.task_meta, L.total]
+    assert offs == sorted(offs)
+    assert B.msa_backward_scratch_bytes(p) >= 4 * 8192 * 64 * (1 + 128) + 2 * 4 * 8192 * 4 * 128
+
+
+@pytest.mark.parametrize("field,value,exc", [
+    ("head_dim", 96, NotImplementedError),
+    ("q_per_kv", 8, NotImplementedError),
+    ("block_size", 128, NotImplementedError),
+    ("topk", 65, NotImplementedError),
+    ("num_chunks", 5, ValueError),
+    ("num_docs", 0, ValueError),
+    ("softmax_scale", 0.0, ValueError),
+])
+def test_bad_problems_are_rejected_on_the_host(field, value, exc):
+    good = B.Problem.make([0, 512], 1, 64, 4)
+    bad = B.Problem(**{**good.__dict__, field: value})
+    with pytest.raises(exc):
+        B.msa_schedule_layout_of(bad)
+
+
+def test_missing_library_raises_unavailable(monkeypatch):
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(ROOT, "no_such_libmsa.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(B.UnavailableError):
+        B.lib()
+    monkeypatch.setattr(B, "_lib", None)   # a failed bind is not cached
+
+
+def test_binding_type_checks():
+    import torch
+    p = B.Problem.make([0, 64], 1, 64, 2)
+    with pytest.raises(TypeError):
+        B._expect(torch.zeros(2, dtype=torch.int64), "cu_seqlens", torch.int32, (2,))
+    with pytest.raises(ValueError):
+        B._expect(torch.zeros(3, dtype=torch.int32), "cu_seqlens", torch.int32, (2,))

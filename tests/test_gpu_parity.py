@@ -1,0 +1,144 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases (the oracle finishes in seconds; several tiles, ragged tails,
+empty documents, junk selection slots, both head dims, both walk regimes and
+the tail walks) are compared element by element.  The five workloads at full
+size are run in the same launch configuration as bench.py: the schedule
+tables are compared bit-exactly, and out/lse/dq/dk/dv on sampled chunks and
+key blocks that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_attention_k2q_amd import binding as B
+from block_sparse_attention_k2q_amd.workloads import make_workload, draw_selection
+from oracle import msa_oracle as O
+
+import msa_testlib as TL
+
+pytestmark = pytest.mark.gpu
+
+
+def _inject_junk(w, seed):
+    """Replace some slots by repeats, out-of-range, non-causal and negative ids."""
+    rng = np.random.default_rng(seed)
+    sel = w.sel.copy()
+    H, C, K = sel.shape
+    layout = O.DocLayout(w.cu_seqlens, w.block)
+    for _ in range(max(4, C // 8)):
+        i, g = int(rng.integers(H)), int(rng.integers(C))
+        d, c = layout.chunk_local(g)
+        s = int(rng.integers(K))
+        kind = int(rng.integers(4))
+        if kind == 0:
+            sel[i, g, s] = sel[i, g, 0]                          # repeat
+        elif kind == 1:
+            sel[i, g, s] = int(layout.nblocks[d]) + int(rng.integers(3))   # past the document
+        elif kind == 2:
+            sel[i, g, s] = min(int(layout.nblocks[d]) - 1, (8 * c) // w.block + 1)  # maybe non-causal
+        else:
+            sel[i, g, s] = -2 - int(rng.integers(5))              # negative, not the empty marker
+    w.sel = sel
+    return w
+
+
+SMALL = {
+    "tiny": lambda: make_workload("tiny"),
+    "ragged_docs_junk": lambda: _inject_junk(make_workload(
+        "tiny", lengths=[200, 0, 77, 512, 9], num_kv_heads=2, head_dim=128, topk=5, seed=11), 3),
+    "d64_two_heads": lambda: make_workload("tiny", lengths=[300, 129], num_kv_heads=2, head_dim=64,
+                                           topk=3, seed=12),
+    "large_walk": lambda: make_workload("tiny", lengths=[2048], num_kv_heads=2, head_dim=128, topk=8,
+                                        seed=13),
+    "zipf_small": lambda: make_workload("tiny", lengths=[4096], num_kv_heads=1, head_dim=128, topk=6,
+                                        selection="zipf", seed=14),
+    "uniform_first_small": lambda: make_workload("tiny", lengths=[1024, 960], num_kv_heads=1,
+                                                 head_dim=128, topk=5, selection="uniform_first",
+                                                 do_std=0.1, seed=15),
+}
+
+
+def _empty_rows_workload():
+    w = make_workload("tiny", lengths=[256, 64], num_kv_heads=1, head_dim=128, topk=3, seed=16)
+    w.sel[0, 5:9] = -1          # four chunks select nothing
+    w.sel[0, 12, :] = -1        # one chunk keeps only an earlier block, not its diagonal
+    w.sel[0, 12, 1] = 0
+    return w
+
+
+SMALL["empty_chunks"] = _empty_rows_workload
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+@pytest.mark.parametrize("num_cus", [None, 7])
+def test_small_cases_full_parity(case, num_cus):
+    w = SMALL[case]()
+    print(f"[case] {case} num_cus={num_cus} T={w.total_tokens} Hkv={w.num_kv_heads} "
+          f"D={w.head_dim} k={w.topk}", flush=True)
+    p = TL.problem_for(w, num_cus)
+    t = TL.to_dev(w)
+    sched = TL.run_schedule(w, p, t)
+    want = TL.compare_schedule(w, p, sched)
+    out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
+    sel_clean = want["sel_clean"]
+    mode = O.backward_dense if w.total_tokens <= 1024 else O.backward_gathered
+    rdq, rdk, rdv, _, rout, rlse = mode(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale)
+    TL.assert_out_lse(out, lse, rout, rlse)
+    TL.assert_grads(dq, dk, dv, rdq, rdk, rdv)
+    # keys no query attends get exactly zero gradient
+    attended = np.zeros(w.total_tokens * w.num_kv_heads, dtype=bool).reshape(w.total_tokens, -1)
+    lay = want["layout"]
+    for i in range(w.num_kv_heads):
+        for g in range(lay.C):
+            d, _, keys = O.chunk_keys(lay, sel_clean, i, g)
+            attended[int(lay.cu[d]) + keys, i] = True
+    assert torch.all(dk.cpu()[torch.from_numpy(~attended)] == 0)
+    assert torch.all(dv.cpu()[torch.from_numpy(~attended)] == 0)
+
+
+FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_configs_sampled(name):
+    print(f"[case] full-size {name}", flush=True)
+    w = make_workload(name)
+    p = TL.problem_for(w)
+    t = TL.to_dev(w)
+    sched = TL.run_schedule(w, p, t)
+    want = TL.compare_schedule(w, p, sched)
+    print(f"[case] {name}: schedule bit-exact, N={int(want['desc'][0])}", flush=True)
+    out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
+    del t
+    lay = want["layout"]
+    rng = np.random.default_rng(7)
+    # sampled chunks: first, last, and random ones, every head
+    chunks = sorted({(int(rng.integers(w.num_kv_heads)), int(g)) for g in
+                     [0, lay.C - 1, *rng.integers(0, lay.C, size=10)]})
+    ref = O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block, w.scale,
+                              chunks=chunks)
+    rows = np.zeros((w.total_tokens, w.num_q_heads), dtype=bool)
+    for i, g in chunks:
+        d, qpos, _ = O.chunk_keys(lay, want["sel_clean"], i, g)
+        rows[np.ix_(int(lay.cu[d]) + qpos, np.arange(16 * i, 16 * i + 16))] = True
+    TL.assert_out_lse(out, lse, ref[4], ref[5], rows=rows)
+    TL.assert_grad("dq", dq, ref[0], rows=rows)
+    # sampled key blocks: every chunk selecting them is recomputed
+    counts = np.diff(want["row_ptr"], axis=1)
+    cand = [(i, r) for i in range(w.num_kv_heads) for r in range(lay.R) if 0 < counts[i, r] <= 160]
+    picks = [cand[j] for j in rng.choice(len(cand), size=min(3, len(cand)), replace=False)]
+    for i, r in picks:
+        sel_chunks = O.chunks_selecting_block(want, i, r)
+        ref = O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block,
+                                  w.scale, chunks=sel_chunks)
+        d = int(lay.row_doc[r])
+        b = r - int(lay.blk_off[d])
+        toks = int(lay.cu[d]) + np.arange(b * w.block, min((b + 1) * w.block, int(lay.lens[d])))
+        kv_rows = np.zeros((w.total_tokens, w.num_kv_heads), dtype=bool)
+        kv_rows[toks, i] = True
+        TL.assert_grad("dk", dk, ref[1], rows=kv_rows)
+        TL.assert_grad("dv", dv, ref[2], rows=kv_rows)
+    # properties at full size
+    assert torch.isfinite(out).all() and torch.isfinite(dq).all()
+    assert torch.isfinite(dk).all() and torch.isfinite(dv).all()
