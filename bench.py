@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA main-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: schedule build (selection cleaning, k2q CSR,
+task table), sparse forward, backward preprocess, backward main kernel,
+backward postprocess.  Workload: one 8192-token document, 4 KV heads x 16
+query heads, head dim 128, key block 64, 8-query chunks, top-k 16.
+
+Prints one JSON line.  ``value`` is useful TFLOP/s of forward + backward:
+every selected (index head, chunk, block) pair counts as one 128 x 64 tile,
+2 contractions forward and 5 backward, each 2*128*64*128 FLOPs.  The
+``roofline`` object is for the backward main kernel (the dominant kernel),
+timed with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "single8k"
+KERNEL_SOURCES = ("block_sparse_attention_k2q_amd/csrc/backward.hip",
+                  "block_sparse_attention_k2q_amd/csrc/msa_device.h")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_main_single8k_hbm_traffic.md")
+
+
+def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
+    tile = 2 * 128 * block * head_dim
+    return 2 * tile, 5 * tile
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per backward-main launch from the committed rocprofv3 --pmc
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(w, sched_host, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload (an even spread of (index head, chunk) pairs, forward +
+    backward of each), reported in useful TFLOP/s."""
+    import numpy as np
+    from oracle import msa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    lay = sched_host["layout"]
+    sel_clean = sched_host["sel_clean"]
+    order = [(i, g) for g in np.linspace(0, lay.C - 1, 256).astype(int) for i in range(w.num_kv_heads)]
+    fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
+    done, pairs, t0 = [], 0, time.perf_counter()
+    for i, g in order:
+        O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale,
+                            chunks=[(i, int(g))])
+        pairs += int((sel_clean[i, g] >= 0).sum())
+        done.append((i, g))
+        if time.perf_counter() - t0 > budget_s and len(done) >= 8:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs * (fwd_f + bwd_f) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(done)} (index head, chunk) pairs of the {WORKLOAD} workload spread evenly "
+                      f"over chunks, {pairs} selected blocks, fp64 forward+backward, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU "
+              "path: the method shards by KV head with no exchange, see the design notes.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from block_sparse_attention_k2q_amd import binding as B
+    from block_sparse_attention_k2q_amd.workloads import make_workload
+
+    dev = torch.device("cuda", 0)
+    num_cus = B.msa_device_check(0)
+    w = make_workload(WORKLOAD)
+    p = B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk, num_cus=num_cus,
+                       softmax_scale=w.scale, block_size=w.block)
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    cu = torch.from_numpy(w.cu_seqlens).to(dev)
+    sel = torch.from_numpy(w.sel).to(dev)
+    sched = B.alloc_schedule(p, dev)
+    scratch = B.alloc_scratch(p, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    names = ("schedule", "forward", "bwd_pre", "bwd_main", "bwd_post")
+
+    def step(ev=None):
+        def mark(x):
+            if ev is not None:
+                ev[x].record()
+        mark(0)
+        B.msa_build_schedule(p, cu, sel, sched)
+        mark(1)
+        B.msa_forward(p, q, k, v, cu, sched, out, lse)
+        mark(2)
+        B.msa_backward_preprocess(p, out, do, scratch)
+        mark(3)
+        B.msa_backward_main(p, q, k, v, do, lse, cu, sched, scratch)
+        mark(4)
+        B.msa_backward_postprocess(p, scratch, dq, dk, dv)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_pairs = int(B.schedule_views(p, sched)["desc"][0].item())
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel = {n: float(np.mean([events[s][j].elapsed_time(events[s][j + 1])
+                                    for s in range(args.steps)])) for j, n in enumerate(names)}
+    ms_step = elapsed * 1e3 / args.steps
+
+    fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
+    value = n_pairs * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+    main_tflops = n_pairs * bwd_f / (per_kernel["bwd_main"] * 1e-3) / 1e12
+    fwd_tflops = n_pairs * fwd_f / (per_kernel["forward"] * 1e-3) / 1e12
+    traffic = measured_traffic()
+
+    result = {
+        "metric": "MSA fwd+bwd useful TFLOP/s and % of bf16 MFMA peak, 1xMI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO, diagonal + uniform block selection)",
+        "config": {"workload": "single8k: 1 document T=8192, 4 KV heads x 16 query heads, D=128, "
+                               "key block 64, chunk 8, top-k 16",
+                   "selected_pairs": n_pairs, "num_cus": num_cus},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {n: round(x, 4) for n, x in per_kernel.items()},
+        "forward_tflops": round(fwd_tflops, 2),
+        "forward_pct_peak": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "bwd_main_tflops": round(main_tflops, 2),
+        "bwd_main_pct_peak": round(100.0 * main_tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
+                     "kernel": "backward_main_kernel<128>",
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import msa_oracle as O
+        sched_host = O.build_schedule(w.sel, w.cu_seqlens, w.block, num_cus)
+        result["cpu_baseline"] = cpu_baseline(w, sched_host)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
