@@ -3,15 +3,16 @@
 
 One step = one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: schedule build (selection cleaning, k2q CSR,
-task table), sparse forward, backward preprocess, backward main kernel,
-backward postprocess.  Workload: one 8192-token document, 4 KV heads x 16
+task table), sparse forward, backward preprocess, backward main kernel
+(KV-parallel: S^T, dP^T, dV, dK), backward dQ kernel (query-parallel, recomputes
+S^T and dP^T), backward postprocess.  Workload: one 8192-token document, 4 KV heads x 16
 query heads, head dim 128, key block 64, 8-query chunks, top-k 16.
 
 Prints one JSON line.  ``value`` is useful TFLOP/s of forward + backward:
 every selected (index head, chunk, block) pair counts as one 128 x 64 tile,
-2 contractions forward and 5 backward, each 2*128*64*128 FLOPs.  The
-``roofline`` object is for the backward main kernel (the dominant kernel),
-timed with HIP events on the stream it is launched on.
+2 contractions forward and 5 backward, each 2*128*64*128 FLOPs; recomputed
+contractions are not counted.  The ``roofline`` object is for the kernel with
+the largest time, timed with HIP events on the stream it is launched on.
 """
 from __future__ import annotations
 
@@ -29,9 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "single8k"
-KERNEL_SOURCES = ("block_sparse_attention_k2q_amd/csrc/backward.hip",
-                  "block_sparse_attention_k2q_amd/csrc/msa_device.h")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bwd_main_single8k_hbm_traffic.md")
+KERNEL_FILES = {"forward": "forward.hip", "bwd_main": "backward.hip", "bwd_dq": "dq.hip"}
+KERNEL_NAMES = {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128>",
+                "bwd_dq": "dq_kernel<128>"}
 
 
 def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
@@ -39,25 +40,25 @@ def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
     return 2 * tile, 5 * tile
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    for rel in (KERNEL_FILES[kernel], "msa_device.h"):
+        with open(os.path.join(ROOT, "block_sparse_attention_k2q_amd", "csrc", rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per backward-main launch from the committed rocprofv3 --pmc
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
     summary, or None when absent or taken on a different kernel source."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(os.path.join(ROOT, "profiles", f"{kernel}_single8k_hbm_traffic.md")) as f:
             text = f.read()
     except OSError:
         return None
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash():
+    if not src or not val or src.group(1) != kernel_source_hash(kernel):
         return None
     return float(val.group(1))
 
@@ -98,6 +99,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dq-mode", choices=("recompute", "atomic"), default="recompute")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU "
@@ -113,8 +115,9 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     num_cus = B.msa_device_check(0)
     w = make_workload(WORKLOAD)
+    dq_mode = B.DQ_ATOMIC_POOL if args.dq_mode == "atomic" else B.DQ_RECOMPUTE
     p = B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk, num_cus=num_cus,
-                       softmax_scale=w.scale, block_size=w.block)
+                       softmax_scale=w.scale, block_size=w.block, dq_mode=dq_mode)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     cu = torch.from_numpy(w.cu_seqlens).to(dev)
     sel = torch.from_numpy(w.sel).to(dev)
@@ -124,7 +127,7 @@ def main() -> int:
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
-    names = ("schedule", "forward", "bwd_pre", "bwd_main", "bwd_post")
+    names = ("schedule", "forward", "bwd_pre", "bwd_main", "bwd_dq", "bwd_post")
 
     def step(ev=None):
         def mark(x):
@@ -139,15 +142,17 @@ def main() -> int:
         mark(3)
         B.msa_backward_main(p, q, k, v, do, lse, cu, sched, scratch)
         mark(4)
-        B.msa_backward_postprocess(p, scratch, dq, dk, dv)
+        B.msa_backward_dq(p, q, k, v, do, lse, cu, sched, scratch, dq)
         mark(5)
+        B.msa_backward_postprocess(p, scratch, dq, dk, dv)
+        mark(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     n_pairs = int(B.schedule_views(p, sched)["desc"][0].item())
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -159,10 +164,16 @@ def main() -> int:
     ms_step = elapsed * 1e3 / args.steps
 
     fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
+    gemm = bwd_f // 5
     value = n_pairs * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
-    main_tflops = n_pairs * bwd_f / (per_kernel["bwd_main"] * 1e-3) / 1e12
-    fwd_tflops = n_pairs * fwd_f / (per_kernel["forward"] * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # useful contractions per pair done by each kernel
+    useful = {"forward": fwd_f, "bwd_main": (5 if dq_mode == B.DQ_ATOMIC_POOL else 4) * gemm,
+              "bwd_dq": (0 if dq_mode == B.DQ_ATOMIC_POOL else 1) * gemm}
+    tflops = {kname: n_pairs * f / (per_kernel[kname] * 1e-3) / 1e12 for kname, f in useful.items()
+              if per_kernel[kname] > 0 and f > 0}
+    bwd_ms = per_kernel["bwd_pre"] + per_kernel["bwd_main"] + per_kernel["bwd_dq"] + per_kernel["bwd_post"]
+    bwd_tflops = n_pairs * bwd_f / (bwd_ms * 1e-3) / 1e12
+    dominant = max(tflops, key=lambda kname: per_kernel[kname])
 
     result = {
         "metric": "MSA fwd+bwd useful TFLOP/s and % of bf16 MFMA peak, 1xMI355X",
@@ -179,17 +190,17 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO, diagonal + uniform block selection)",
         "config": {"workload": "single8k: 1 document T=8192, 4 KV heads x 16 query heads, D=128, "
                                "key block 64, chunk 8, top-k 16",
-                   "selected_pairs": n_pairs, "num_cus": num_cus},
+                   "selected_pairs": n_pairs, "num_cus": num_cus, "dq_mode": args.dq_mode},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(x, 4) for n, x in per_kernel.items()},
-        "forward_tflops": round(fwd_tflops, 2),
-        "forward_pct_peak": round(100.0 * fwd_tflops / PEAK_BF16_TFLOPS, 2),
-        "bwd_main_tflops": round(main_tflops, 2),
-        "bwd_main_pct_peak": round(100.0 * main_tflops / PEAK_BF16_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(main_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(main_tflops / PEAK_BF16_TFLOPS, 4),
-                     "kernel": "backward_main_kernel<128>",
-                     "traffic": traffic},
+        "kernels_useful_tflops": {n: round(x, 2) for n, x in tflops.items()},
+        "kernels_pct_peak": {n: round(100.0 * x / PEAK_BF16_TFLOPS, 2) for n, x in tflops.items()},
+        "forward_pct_peak": round(100.0 * tflops["forward"] / PEAK_BF16_TFLOPS, 2),
+        "backward_useful_tflops": round(bwd_tflops, 2),
+        "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops[dominant], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops[dominant] / PEAK_BF16_TFLOPS, 4),
+                     "kernel": KERNEL_NAMES[dominant], "traffic": measured_traffic(dominant)},
     }
     if not args.no_cpu_baseline:
         from oracle import msa_oracle as O

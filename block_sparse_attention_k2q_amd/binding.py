@@ -25,12 +25,13 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_HIP = range(6)
 SCHED_ERR_DROPPED, SCHED_ERR_GEOMETRY = 0, 1
+DQ_RECOMPUTE, DQ_ATOMIC_POOL = 0, 1
 MAX_DOC_CHUNKS = 1 << 18
 
 EXPORTED = (
     "msa_device_check", "msa_schedule_layout_of", "msa_build_schedule", "msa_forward",
     "msa_backward_scratch_bytes", "msa_backward", "msa_backward_preprocess", "msa_backward_main",
-    "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
+    "msa_backward_dq", "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
 )
 
 
@@ -42,7 +43,7 @@ class MSAProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "total_tokens", "num_docs", "num_kv_heads", "q_per_kv", "head_dim", "block_size",
         "query_chunk", "topk", "num_chunks", "num_kblocks", "max_doc_chunks", "num_cus")] + [
-        ("softmax_scale", ctypes.c_float)]
+        ("softmax_scale", ctypes.c_float), ("dq_mode", ctypes.c_int32)]
 
 
 class MSAScheduleLayout(ctypes.Structure):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "msa_backward": ([P, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp, vp, vp], ctypes.c_int),
             "msa_backward_preprocess": ([P, vp, vp, vp, vp], ctypes.c_int),
             "msa_backward_main": ([P, vp, vp, vp, vp, vp, i32p, i32p, vp, vp], ctypes.c_int),
+            "msa_backward_dq": ([P, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp], ctypes.c_int),
             "msa_backward_postprocess": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
             "msa_grid_launch_bound": ([ctypes.c_int64, ctypes.c_int32], ctypes.c_int64),
             "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -136,10 +138,12 @@ class Problem:
     q_per_kv: int = 16
     block_size: int = 64
     query_chunk: int = 8
+    dq_mode: int = DQ_RECOMPUTE
 
     @staticmethod
     def make(cu_seqlens, num_kv_heads: int, head_dim: int, topk: int, num_cus: int = 256,
-             softmax_scale: Optional[float] = None, block_size: int = 64) -> "Problem":
+             softmax_scale: Optional[float] = None, block_size: int = 64,
+             dq_mode: int = DQ_RECOMPUTE) -> "Problem":
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         lens = np.diff(cu)
         nch = -(-lens // 8)
@@ -148,7 +152,7 @@ class Problem:
                        num_kblocks=int((-(-lens // block_size)).sum()),
                        max_doc_chunks=int(nch.max(initial=0)), num_cus=int(num_cus),
                        softmax_scale=float(head_dim ** -0.5 if softmax_scale is None else softmax_scale),
-                       block_size=int(block_size))
+                       block_size=int(block_size), dq_mode=int(dq_mode))
 
     @property
     def num_q_heads(self) -> int:
@@ -162,7 +166,7 @@ class Problem:
         return MSAProblem(self.total_tokens, self.num_docs, self.num_kv_heads, self.q_per_kv,
                           self.head_dim, self.block_size, self.query_chunk, self.topk,
                           self.num_chunks, self.num_kblocks, self.max_doc_chunks, self.num_cus,
-                          self.softmax_scale)
+                          self.softmax_scale, self.dq_mode)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -268,6 +272,16 @@ def msa_backward_main(p: Problem, q, k, v, dout, lse, cu_seqlens, sched, scratch
     _check(lib().msa_backward_main(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                                    _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _stream(stream)),
            "msa_backward_main")
+
+
+def msa_backward_dq(p: Problem, q, k, v, dout, lse, cu_seqlens, sched, scratch, dq, stream=None) -> None:
+    _check_bwd_inputs(p, q, k, v, None, dout, lse, cu_seqlens, sched, scratch)
+    T, hq, D = p.total_tokens, p.num_q_heads, p.head_dim
+    _expect(dq, "dq", torch.bfloat16, (T, hq, D))
+    ps = p.c_struct()
+    _check(lib().msa_backward_dq(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                 _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq), _stream(stream)),
+           "msa_backward_dq")
 
 
 def msa_backward_postprocess(p: Problem, scratch, dq, dk, dv, stream=None) -> None:

@@ -40,6 +40,7 @@ int check_problem(const msa_problem* p) {
       p->max_doc_chunks > p->num_chunks || (p->num_chunks > 0 && p->max_doc_chunks < 1))
     return MSA_ERR_SHAPE;
   if (!(p->softmax_scale > 0.f)) return MSA_ERR_INVALID;
+  if (p->dq_mode != MSA_DQ_RECOMPUTE && p->dq_mode != MSA_DQ_ATOMIC_POOL) return MSA_ERR_INVALID;
   return MSA_OK;
 }
 
@@ -126,6 +127,22 @@ int msa_backward_main(const msa_problem* p, const void* q, const void* k, const 
                                               (hipStream_t)stream));
 }
 
+int msa_backward_dq(const msa_problem* p, const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, const int32_t* cu_seqlens,
+                    const int32_t* sched, const void* scratch, void* dq, void* stream) {
+  const int st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (!cu_seqlens || !sched ||
+      (p->total_tokens > 0 && (!q || !k || !v || !dout || !lse || !scratch || !dq)))
+    return MSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(scratch) ||
+      !aligned16(sched) || !aligned16(dq))
+    return MSA_ERR_ALIGN;
+  const msa_schedule_layout L = msa::schedule_layout(*p);
+  return hip_status(msa::launch_backward_dq(*p, q, k, v, dout, lse, cu_seqlens, sched, L, scratch, dq,
+                                            (hipStream_t)stream));
+}
+
 int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk, void* dv,
                              void* stream) {
   const int st = check_problem(p);
@@ -141,6 +158,8 @@ int msa_backward(const msa_problem* p, const void* q, const void* k, const void*
   int st = msa_backward_preprocess(p, out, dout, scratch, stream);
   if (st != MSA_OK) return st;
   st = msa_backward_main(p, q, k, v, dout, lse, cu_seqlens, sched, scratch, stream);
+  if (st != MSA_OK) return st;
+  st = msa_backward_dq(p, q, k, v, dout, lse, cu_seqlens, sched, scratch, dq, stream);
   if (st != MSA_OK) return st;
   return msa_backward_postprocess(p, scratch, dq, dk, dv, stream);
 }

@@ -33,6 +33,7 @@ namespace msa {
 namespace {
 
 constexpr int kBwdThreads = 256;
+constexpr int kMaxWalk = 64;   // ROWS_PER_CTA_LARGE: longest walk a workgroup takes
 
 // ---------------------------------------------------------------------------
 // Preprocess: Delta = rowsum(dO * O) in fp32; zero the dQ pool and dK/dV.
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const bf16* __restrict_
                                                          float* __restrict__ delta,
                                                          float* __restrict__ dq_pool,
                                                          float* __restrict__ dkv, int64_t n_vec,
-                                                         int64_t n_dkv_vec) {
+                                                         int64_t n_dkv_vec, int zero_pool) {
   constexpr int LPR = D / 8;  // lanes per (token, head) row
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x < n_dkv_vec) {
@@ -60,9 +61,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const bf16* __restrict_
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off, 64);
   if ((x % LPR) == 0) delta[x / LPR] = s;
-  floatx4* p = reinterpret_cast<floatx4*>(dq_pool) + 2 * x;
-  p[0] = floatx4{};
-  p[1] = floatx4{};
+  if (zero_pool) {
+    floatx4* p = reinterpret_cast<floatx4*>(dq_pool) + 2 * x;
+    p[0] = floatx4{};
+    p[1] = floatx4{};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -108,9 +111,10 @@ struct BwdSmem {
   bf16 ds[kTileM * LDP];
   float lse2[kTileM];
   float delta[kTileM];
+  int meta[kMaxWalk][8];   // per walked task: i, r, qb, qc, d, b, tok0, len
 };
 
-template <int D>
+template <int D, bool ATOMIC_DQ>
 __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -164,23 +168,67 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     for (int x = 0; x < OUT_TILES; ++x) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        // Keys past the document end hold exact zeros (zero K/V rows, masked
+        // P); they are sent to the block's first key so the atomics need no branch.
         const int key = 32 * own_mt[x] + 8 * (j >> 2) + 4 * h + (j & 3);
-        const int kpos = cur_b * kBlock + key;
-        if (kpos < cur_len) {
-          const int64_t off = ((int64_t)(cur_tok0 + kpos) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
-          atomicAdd(dv_acc + off, acc_dv[x][j]);
-          atomicAdd(dk_acc + off, acc_dk[x][j]);
-        }
+        const int kpos = cur_b * kBlock + (cur_b * kBlock + key < cur_len ? key : 0);
+        const int64_t off = ((int64_t)(cur_tok0 + kpos) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
+        atomicAdd(dv_acc + off, acc_dv[x][j]);
+        atomicAdd(dk_acc + off, acc_dk[x][j]);
       }
     }
   };
 
+  // The walk's task rows, with their document start and length, once into LDS.
+  const int nrows = hi - lo;
+  for (int e = threadIdx.x; e < nrows; e += kBwdThreads) {
+    const int32_t* tm = task_meta + (int64_t)(lo + e) * 6;
+    int* m = sm.meta[e];
+#pragma unroll
+    for (int x = 0; x < 6; ++x) m[x] = tm[x];
+    const int d = tm[4];
+    const int t0 = cu[d];
+    m[6] = t0;
+    m[7] = cu[d + 1] - t0;
+  }
+  lds_barrier();
+
+  // Register prefetch of one tile: Q and dO rows (m = token * 16 + head; zero
+  // past the document end) and the raw LSE (threads 0..127) or Delta
+  // (threads 128..255) of row m.  Nothing here consumes the loaded values, so
+  // the loads stay in flight while the current tile computes.
+  constexpr int PFV = kTileM * VEC / kBwdThreads;
+  u32x4 pq_[PFV], po_[PFV];
+  float pscal = 0.f;
+  const bool is_lse_thread = threadIdx.x < kTileM;
+  auto prefetch = [&](int e) {
+    const int* m = sm.meta[e];
+    const int i = m[0], qb = m[2], qc = m[3], tok0 = m[6];
+#pragma unroll
+    for (int x = 0; x < PFV; ++x) {
+      const int idx = threadIdx.x + x * kBwdThreads;
+      const int mm = idx / VEC, col = (idx % VEC) * 8;
+      const int j = mm >> 4, hh = mm & 15;
+      if (j < qc) {
+        const int64_t off = ((int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + hh) * D + col;
+        pq_[x] = *reinterpret_cast<const u32x4*>(q + off);
+        po_[x] = *reinterpret_cast<const u32x4*>(dout + off);
+      } else {
+        pq_[x] = u32x4{0, 0, 0, 0};
+        po_[x] = u32x4{0, 0, 0, 0};
+      }
+    }
+    const int mm = threadIdx.x & (kTileM - 1), j = mm >> 4, hh = mm & 15;
+    const int64_t rowi = (int64_t)(tok0 + qb + min(j, qc - 1)) * Hq + kQPerKV * i + hh;
+    pscal = is_lse_thread ? lse[rowi] : delta[rowi];
+  };
+  if (nrows > 0) prefetch(0);
+
   for (int row = lo; row < hi; ++row) {
-    const int32_t* tm = task_meta + (int64_t)row * 6;
-    const int i = tm[0], r = tm[1], qb = tm[2], qc = tm[3], d = tm[4], b = tm[5];
-    const int tok0 = cu[d];
-    const int len = cu[d + 1] - tok0;
-    __syncthreads();  // previous tile fully consumed
+    const int* mrow = sm.meta[row - lo];
+    const int i = mrow[0], r = mrow[1], qb = mrow[2], qc = mrow[3], b = mrow[5];
+    const int tok0 = mrow[6], len = mrow[7];
+    lds_barrier();  // previous tile fully consumed
     if (i != cur_i || r != cur_r) {
       if (cur_i >= 0) flush();
 #pragma unroll
@@ -202,53 +250,58 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
         *reinterpret_cast<u32x4*>(&sm.v[kr * LDK + col]) = vv;
       }
     }
-    // Q / dO tile rows m = token * 16 + head; rows past the document end are zero.
-    for (int e = threadIdx.x; e < kTileM * VEC; e += kBwdThreads) {
-      const int m = e / VEC, col = (e % VEC) * 8;
-      const int j = m >> 4, hh = m & 15;
-      u32x4 qv = {0, 0, 0, 0}, ov = {0, 0, 0, 0};
-      if (j < qc) {
-        const int64_t off = ((int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + hh) * D + col;
-        qv = *reinterpret_cast<const u32x4*>(q + off);
-        ov = *reinterpret_cast<const u32x4*>(dout + off);
-      }
-      *reinterpret_cast<u32x4*>(&sm.q[m * LDK + col]) = qv;
-      *reinterpret_cast<u32x4*>(&sm.dout[m * LDK + col]) = ov;
+#pragma unroll
+    for (int x = 0; x < PFV; ++x) {
+      const int idx = threadIdx.x + x * kBwdThreads;
+      const int mm = idx / VEC, col = (idx % VEC) * 8;
+      *reinterpret_cast<u32x4*>(&sm.q[mm * LDK + col]) = pq_[x];
+      *reinterpret_cast<u32x4*>(&sm.dout[mm * LDK + col]) = po_[x];
     }
-    if (threadIdx.x < kTileM) {
-      const int m = threadIdx.x, j = m >> 4, hh = m & 15;
-      float l2 = INFINITY, dl = 0.f;
-      if (j < qc) {
-        const int64_t rowi = (int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + hh;
-        const float lv = lse[rowi];
-        l2 = (lv == -INFINITY) ? INFINITY : lv * kLog2e;
-        dl = delta[rowi];
-      }
-      sm.lse2[m] = l2;
-      sm.delta[m] = dl;
+    {
+      // Rows past the document end get LSE = +inf (so P = 0) and Delta = 0.
+      const int mm = threadIdx.x & (kTileM - 1);
+      const bool valid = (mm >> 4) < qc;
+      if (is_lse_thread)
+        sm.lse2[mm] = (valid && pscal != -INFINITY) ? pscal * kLog2e : INFINITY;
+      else
+        sm.delta[mm] = valid ? pscal : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
+    if (row + 1 < hi) prefetch(row + 1 - lo);
 
     // --- S^T and dP^T for this wave's 32 query rows -------------------------
+    // Operands of k step s+1 are read from LDS while step s runs on the MFMA.
     const int mq = 32 * w + n32;   // this lane's query row in the tile
     floatx16 st[2] = {floatx16{}, floatx16{}};
     floatx16 dpt[2] = {floatx16{}, floatx16{}};
+    {
+      bf16x8 bq[2], bo[2], ak[2][2], av[2][2];
+      auto load_step = [&](int s, int slot) {
+        bq[slot] = load_bf16x8(&sm.q[mq * LDK + 16 * s + 8 * h]);
+        bo[slot] = load_bf16x8(&sm.dout[mq * LDK + 16 * s + 8 * h]);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 bq = load_bf16x8(&sm.q[mq * LDK + 16 * s + 8 * h]);
-      const bf16x8 bo = load_bf16x8(&sm.dout[mq * LDK + 16 * s + 8 * h]);
+        for (int t = 0; t < 2; ++t) {
+          ak[slot][t] = load_bf16x8(&sm.k[(32 * t + n32) * LDK + 16 * s + 8 * h]);
+          av[slot][t] = load_bf16x8(&sm.v[(32 * t + n32) * LDK + 16 * s + 8 * h]);
+        }
+      };
+      load_step(0, 0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 ak = load_bf16x8(&sm.k[(32 * t + n32) * LDK + 16 * s + 8 * h]);
-        const bf16x8 av = load_bf16x8(&sm.v[(32 * t + n32) * LDK + 16 * s + 8 * h]);
-        st[t] = mfma32(ak, bq, st[t]);
-        dpt[t] = mfma32(av, bo, dpt[t]);
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_step(s + 1, (s + 1) & 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          st[t] = mfma32(ak[s & 1][t], bq[s & 1], st[t]);
+          dpt[t] = mfma32(av[s & 1][t], bo[s & 1], dpt[t]);
+        }
       }
     }
     const float l2 = sm.lse2[mq];
     const float dl = sm.delta[mq];
+    // Keys of this block at tile offset <= klim are visible to this query
+    // (causal within the diagonal block, and inside the document).
     const int pq = qb + (mq >> 4);
-    const bool need_mask = (b + 1) * kBlock - 1 > qb;
+    const int klim = min(pq, len - 1) - b * kBlock;
     bf16x8 dsa[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -258,11 +311,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int j = 4 * jg + rr;
+          const int key = 32 * t + 8 * jg + 4 * h + rr;
           float pv = fast_exp2(st[t][j] * c2 - l2);
-          if (need_mask) {
-            const int kpos = b * kBlock + 32 * t + 8 * jg + 4 * h + rr;
-            if (kpos > pq || kpos >= len) pv = 0.f;
-          }
+          pv = key <= klim ? pv : 0.f;
           const float dsv = pv * (dpt[t][j] - dl);
           p4[rr] = (bf16)pv;
           d4[rr] = (bf16)dsv;
@@ -274,50 +325,68 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
       }
     }
 
-    // --- dQ = dS K (32 query rows x D) -> fp32 pool ---------------------------
-    {
+    // --- dQ = dS K (32 query rows x D) -> fp32 pool (atomic-pool mode) --------
+    if constexpr (ATOMIC_DQ) {
       floatx16 dq[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) dq[t] = floatx16{};
+      bf16x8 bk[2][NT];
+      auto load_k = [&](int u, int slot) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          bk[slot][t] = lds_tr_operand(sm.k, LDK, 32 * t, lane, 16 * u, 16 * u + 4, 16 * u + 8,
+                                       16 * u + 12);
+      };
+      load_k(0, 0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) load_k(u + 1, (u + 1) & 1);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const bf16x8 bk = lds_tr_operand(sm.k, LDK, 32 * t, lane, 16 * u, 16 * u + 4, 16 * u + 8,
-                                           16 * u + 12);
-          dq[t] = mfma32(dsa[u], bk, dq[t]);
-        }
+        for (int t = 0; t < NT; ++t) dq[t] = mfma32(dsa[u], bk[u & 1][t], dq[t]);
       }
-      // accumulator: column = d (lane), rows = query rows 8(j/4) + 4h + j%4 of this wave
+      // Accumulator: column = d (lane), rows = query rows 8(j/4) + 4h + j%4 of
+      // this wave.  Rows past the document end hold exact zeros (their P and
+      // dS are 0); they are sent to the tile's first row, which always exists,
+      // so the atomics need no branch.
+      const int64_t row0 = (int64_t)(tok0 + qb) * Hq + kQPerKV * i;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int m = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
         const int jt = m >> 4, hh = m & 15;
-        if (jt < qc) {
-          float* dst = dq_pool + ((int64_t)(tok0 + qb + jt) * Hq + kQPerKV * i + hh) * D + n32;
+        const int64_t rowm = jt < qc ? row0 + (int64_t)jt * Hq + hh : row0;
+        float* dst = dq_pool + rowm * D + n32;
 #pragma unroll
-          for (int t = 0; t < NT; ++t) atomicAdd(dst + 32 * t, dq[t][j]);
-        }
+        for (int t = 0; t < NT; ++t) atomicAdd(dst + 32 * t, dq[t][j]);
       }
     }
-    __syncthreads();  // P, dS complete in LDS
+    lds_barrier();  // P, dS complete in LDS
 
     // --- dV += P^T dO, dK += dS^T Q over all 128 query rows -------------------
+    {
+      bf16x8 ap[2][OUT_TILES], ad[2][OUT_TILES], bo[2][OUT_TILES], bq[2][OUT_TILES];
+      auto load_u = [&](int u, int slot) {
 #pragma unroll
-    for (int u = 0; u < kTileM / 16; ++u) {
+        for (int x = 0; x < OUT_TILES; ++x) {
+          const int mt = own_mt[x], nt = own_nt[x];
+          ap[slot][x] = lds_tr_operand(sm.p, LDP, 32 * mt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                       16 * u + 12);
+          bo[slot][x] = lds_tr_operand(sm.dout, LDK, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                       16 * u + 12);
+          ad[slot][x] = lds_tr_operand(sm.ds, LDP, 32 * mt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                       16 * u + 12);
+          bq[slot][x] = lds_tr_operand(sm.q, LDK, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                       16 * u + 12);
+        }
+      };
+      load_u(0, 0);
 #pragma unroll
-      for (int x = 0; x < OUT_TILES; ++x) {
-        const int mt = own_mt[x], nt = own_nt[x];
-        const bf16x8 ap = lds_tr_operand(sm.p, LDP, 32 * mt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
-                                         16 * u + 12);
-        const bf16x8 bo = lds_tr_operand(sm.dout, LDK, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
-                                         16 * u + 12);
-        acc_dv[x] = mfma32(ap, bo, acc_dv[x]);
-        const bf16x8 ad = lds_tr_operand(sm.ds, LDP, 32 * mt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
-                                         16 * u + 12);
-        const bf16x8 bq = lds_tr_operand(sm.q, LDK, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
-                                         16 * u + 12);
-        acc_dk[x] = mfma32(ad, bq, acc_dk[x]);
+      for (int u = 0; u < kTileM / 16; ++u) {
+        if (u + 1 < kTileM / 16) load_u(u + 1, (u + 1) & 1);
+#pragma unroll
+        for (int x = 0; x < OUT_TILES; ++x) {
+          acc_dv[x] = mfma32(ap[u & 1][x], bo[u & 1][x], acc_dv[x]);
+          acc_dk[x] = mfma32(ad[u & 1][x], bq[u & 1][x], acc_dk[x]);
+        }
       }
     }
   }
@@ -333,14 +402,14 @@ hipError_t launch_backward_preprocess(const msa_problem& p, const void* out, con
   const int64_t hq = (int64_t)p.num_kv_heads * p.q_per_kv;
   const int64_t n_vec = (int64_t)p.total_tokens * hq * p.head_dim / 8;
   // dK and dV accumulators are adjacent: zero both as one range.
-  const int64_t n_dkv_vec = (int64_t)(L.total - L.dk_acc) / 32;
+  const int64_t n_dkv_vec = (int64_t)(L.dq_pool - L.dk_acc) / 32;
   const int64_t n = n_vec > n_dkv_vec ? n_vec : n_dkv_vec;
   if (n == 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + 255) / 256);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const bf16*)out, (const bf16*)dout,
                        (float*)(base + L.delta), (float*)(base + L.dq_pool), (float*)(base + L.dk_acc),
-                       n_vec, n_dkv_vec);
+                       n_vec, n_dkv_vec, p.dq_mode == MSA_DQ_ATOMIC_POOL ? 1 : 0);
   };
   if (p.head_dim == 128) go(preprocess_kernel<128>);
   else go(preprocess_kernel<64>);
@@ -366,8 +435,13 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        (float*)(base + S.dv_acc), p.num_kv_heads, p.softmax_scale);
     return hipGetLastError();
   };
-  if (p.head_dim == 128) return go(backward_main_kernel<128>, sizeof(BwdSmem<128>));
-  return go(backward_main_kernel<64>, sizeof(BwdSmem<64>));
+  const bool atomic_dq = p.dq_mode == MSA_DQ_ATOMIC_POOL;
+  if (p.head_dim == 128) {
+    return atomic_dq ? go(backward_main_kernel<128, true>, sizeof(BwdSmem<128>))
+                     : go(backward_main_kernel<128, false>, sizeof(BwdSmem<128>));
+  }
+  return atomic_dq ? go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>))
+                   : go(backward_main_kernel<64, false>, sizeof(BwdSmem<64>));
 }
 
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
@@ -375,7 +449,8 @@ hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch
   const BackwardScratch L = backward_scratch_layout(p);
   const uint8_t* base = (const uint8_t*)scratch;
   const int64_t hq = (int64_t)p.num_kv_heads * p.q_per_kv;
-  const int64_t n_q_vec = (int64_t)p.total_tokens * hq * p.head_dim / 8;
+  const int64_t n_q_vec =
+      p.dq_mode == MSA_DQ_ATOMIC_POOL ? (int64_t)p.total_tokens * hq * p.head_dim / 8 : 0;
   const int64_t n_kv_vec = (int64_t)p.total_tokens * p.num_kv_heads * p.head_dim / 8;
   const int64_t n = n_q_vec > n_kv_vec ? n_q_vec : n_kv_vec;
   if (n == 0) return hipSuccess;

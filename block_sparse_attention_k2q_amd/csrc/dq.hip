@@ -1,0 +1,228 @@
+// Query-parallel dQ kernel of the MSA backward on gfx950 (MSA_DQ_RECOMPUTE).
+//
+// dQ_p = scale * sum_j dS_pj k_j with dS = P (dP - Delta), P = exp(s - LSE)
+// (msa_backward_sm100 page: the dQ^T contraction; kernels page: Delta from
+// the backward preprocess).  On MI355X, fp32 global atomics execute beyond
+// the L2 at a rate that cannot keep up with one 128 x D atomic tile per
+// (chunk, block) pair, so instead of scattering dQ from the KV-parallel
+// kernel this kernel walks each chunk's kept blocks, like the forward, and
+// keeps dQ in registers:
+//
+//  * one workgroup per (chunk, index head), 4 waves x 32 query rows; Q and
+//    dO rows of the tile stay in registers as MFMA B operands;
+//  * per kept block: K and V staged in LDS (next block prefetched into
+//    registers), S^T = K Q^T and dP^T = V dO^T (keys x queries),
+//    P^T = exp2(S^T * scale * log2e - LSE * log2e) with the causal mask,
+//    dS^T = P^T (dP^T - Delta), and dQ^T += K^T dS^T with dS^T taken straight
+//    from the accumulators and K^T read through the LDS transpose load;
+//  * dq = bf16(scale * dQ) written once.
+#include "msa_device.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+namespace {
+
+constexpr int kDqThreads = 256;
+
+template <int D>
+struct DqSmem {
+  static constexpr int LDK = D + 8;
+  bf16 k[kBlock * LDK];
+  bf16 v[kBlock * LDK];
+  int blocks[64];
+  int nblocks;
+};
+
+template <int D>
+__global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
+    const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
+    const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv, int C, int K, float scale) {
+  using S = DqSmem<D>;
+  constexpr int LDK = S::LDK;
+  constexpr int KS = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int VEC = D / 8;
+  constexpr int PF = kBlock * VEC / kDqThreads;
+  __shared__ __attribute__((aligned(16))) S sm;
+
+  if (err[1]) return;
+  const int i = blockIdx.x % Hkv;
+  const int g = blockIdx.x / Hkv;
+  const int d = chunk_doc[g];
+  const int c = g - doc_chunk_off[d];
+  const int tok0 = cu[d];
+  const int len = cu[d + 1] - tok0;
+  const int p0 = kChunk * c;
+  const int qcount = min(kChunk, len - p0);
+  const int Hq = Hkv * kQPerKV;
+
+  if (threadIdx.x == 0) {
+    int n = 0;
+    const int32_t* row = sel_clean + ((int64_t)i * C + g) * K;
+    for (int s = 0; s < K; ++s) {
+      const int b = row[s];
+      if (b >= 0) sm.blocks[n++] = b;
+    }
+    sm.nblocks = n;
+  }
+
+  const int w = wave_id(), lane = lane_id();
+  const int n32 = lane & 31, h = lane >> 5;
+  const int jq = 2 * w + (n32 >> 4);
+  const int hh = n32 & 15;
+  const bool qvalid = jq < qcount;
+  const int pq = p0 + jq;
+  const int64_t qrow = (int64_t)(tok0 + p0 + min(jq, qcount - 1)) * Hq + kQPerKV * i + hh;
+
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = qvalid ? load_bf16x8(q + qrow * D + 16 * s + 8 * h) : bf16x8{};
+    of[s] = qvalid ? load_bf16x8(dout + qrow * D + 16 * s + 8 * h) : bf16x8{};
+  }
+  const float lv = lse[qrow];
+  const float l2 = (qvalid && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+  const float dl = qvalid ? delta[qrow] : 0.f;
+  const float c2 = scale * kLog2e;
+
+  floatx16 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = floatx16{};
+
+  lds_barrier();
+  const int nblk = sm.nblocks;
+
+  u32x4 pk[PF], pv[PF];
+  auto prefetch = [&](int b) {
+#pragma unroll
+    for (int x = 0; x < PF; ++x) {
+      const int e = threadIdx.x + x * kDqThreads;
+      const int row = e / VEC, col = (e % VEC) * 8;
+      const int key = b * kBlock + row;
+      if (key < len) {
+        const int64_t off = ((int64_t)(tok0 + key) * Hkv + i) * D + col;
+        pk[x] = *reinterpret_cast<const u32x4*>(k + off);
+        pv[x] = *reinterpret_cast<const u32x4*>(v + off);
+      } else {
+        pk[x] = u32x4{0, 0, 0, 0};
+        pv[x] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  if (nblk > 0) prefetch(sm.blocks[0]);
+
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int b = sm.blocks[bi];
+    lds_barrier();
+#pragma unroll
+    for (int x = 0; x < PF; ++x) {
+      const int e = threadIdx.x + x * kDqThreads;
+      const int row = e / VEC, col = (e % VEC) * 8;
+      *reinterpret_cast<u32x4*>(&sm.k[row * LDK + col]) = pk[x];
+      *reinterpret_cast<u32x4*>(&sm.v[row * LDK + col]) = pv[x];
+    }
+    lds_barrier();
+    if (bi + 1 < nblk) prefetch(sm.blocks[bi + 1]);
+
+    // S^T = K Q^T and dP^T = V dO^T, operands of step s+1 read during step s.
+    floatx16 st[2] = {floatx16{}, floatx16{}};
+    floatx16 dpt[2] = {floatx16{}, floatx16{}};
+    {
+      bf16x8 ak[2][2], av[2][2];
+      auto load_step = [&](int s, int slot) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          ak[slot][t] = load_bf16x8(&sm.k[(32 * t + n32) * LDK + 16 * s + 8 * h]);
+          av[slot][t] = load_bf16x8(&sm.v[(32 * t + n32) * LDK + 16 * s + 8 * h]);
+        }
+      };
+      load_step(0, 0);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_step(s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          st[t] = mfma32(ak[s & 1][t], qf[s], st[t]);
+          dpt[t] = mfma32(av[s & 1][t], of[s], dpt[t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // dS^T in bf16, packed as B operands of dQ^T (k step u = keys 16u..16u+15).
+    const int klim = min(pq, len - 1) - b * kBlock;
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
+        float pv_ = fast_exp2(st[t][j] * c2 - l2);
+        pv_ = key <= klim ? pv_ : 0.f;
+        dsb[2 * t + (j >> 3)][j & 7] = (bf16)(pv_ * (dpt[t][j] - dl));
+      }
+    }
+
+    // dQ^T += K^T dS^T.
+    {
+      bf16x8 ak[2][NT];
+      auto load_u = [&](int u, int slot) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          ak[slot][t] = lds_tr_operand(sm.k, LDK, 32 * t, lane, 16 * u, 16 * u + 4, 16 * u + 8,
+                                       16 * u + 12);
+      };
+      load_u(0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (u + 1 < 4) load_u(u + 1, (u + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma32(ak[u & 1][t], dsb[u], acc[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  if (!qvalid) return;
+  bf16* orow = dq + qrow * D;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      bf16x4 v4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v4[r] = (bf16)(acc[t][4 * jg + r] * scale);
+      store_bf16x4(orow + 32 * t + 8 * jg + 4 * h, v4);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const int32_t* cu,
+                              const int32_t* sched, const msa_schedule_layout& L, const void* scratch,
+                              void* dq, hipStream_t stream) {
+  if (p.dq_mode != MSA_DQ_RECOMPUTE) return hipSuccess;
+  const int64_t nwg = (int64_t)p.num_chunks * p.num_kv_heads;
+  if (nwg == 0) return hipSuccess;
+  const BackwardScratch S = backward_scratch_layout(p);
+  const float* delta = (const float*)((const uint8_t*)scratch + S.delta);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta, cu,
+                       sched + L.chunk_doc, sched + L.doc_chunk_off, sched + L.sel_clean, sched + L.err,
+                       (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
+  };
+  if (p.head_dim == 128) go(dq_kernel<128>);
+  else go(dq_kernel<64>);
+  return hipGetLastError();
+}
+
+}  // namespace msa

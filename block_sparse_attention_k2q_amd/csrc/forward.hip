@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
   float m = -INFINITY, l = 0.f;
   const float c2 = scale * kLog2e;
 
-  __syncthreads();
+  lds_barrier();
   const int nblk = sm.nblocks;
 
   // Register prefetch of one block's K and V rows (zero past the document end).
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
 
   for (int bi = 0; bi < nblk; ++bi) {
     const int b = sm.blocks[bi];
-    __syncthreads();  // all waves are done with the previous block's tiles
+    lds_barrier();  // all waves are done with the previous block's tiles
 #pragma unroll
     for (int x = 0; x < PF; ++x) {
       const int e = threadIdx.x + x * kFwdThreads;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
       *reinterpret_cast<u32x4*>(&sm.k[row * LDK + col]) = pk[x];
       *reinterpret_cast<u32x4*>(&sm.v[row * LDV + col]) = pv[x];
     }
-    __syncthreads();
+    lds_barrier();
     if (bi + 1 < nblk) prefetch(sm.blocks[bi + 1]);
 
     // S^T = K Q^T: two 32-key tiles.

@@ -90,6 +90,16 @@ __device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes every wave wait for all of its outstanding global loads
+// and atomics at each barrier; the tiles here share data through LDS only, so
+// prefetch loads and fire-and-forget atomics stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);

@@ -43,9 +43,11 @@ inline int64_t grid_launch_bound(int64_t cap, int num_cus) {
   return (small > large ? small : large) + num_cus;
 }
 
-// Scratch layout of the backward (bytes, 256-aligned): Delta, dQ pool, dK, dV.
+// Scratch layout of the backward (bytes, 256-aligned): Delta, dK, dV
+// accumulators (adjacent, so one range clears both), and the dQ pool in
+// MSA_DQ_ATOMIC_POOL mode (dq_pool == total otherwise).
 struct BackwardScratch {
-  size_t delta, dq_pool, dk_acc, dv_acc, total;
+  size_t delta, dk_acc, dv_acc, dq_pool, total;
 };
 inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -54,9 +56,10 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   BackwardScratch s;
   size_t o = 0;
   s.delta = o; o = a256(o + 4 * T * hq);
-  s.dq_pool = o; o = a256(o + 4 * T * hq * D);
   s.dk_acc = o; o = a256(o + 4 * T * hkv * D);
   s.dv_acc = o; o = a256(o + 4 * T * hkv * D);
+  s.dq_pool = o;
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL) o = a256(o + 4 * T * hq * D);
   s.total = o;
   return s;
 }
@@ -72,6 +75,10 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                                 const void* dout, const float* lse, const int32_t* cu,
                                 const int32_t* sched, const msa_schedule_layout& L, void* scratch,
                                 hipStream_t stream);
+hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k, const void* v,
+                              const void* dout, const float* lse, const int32_t* cu,
+                              const int32_t* sched, const msa_schedule_layout& L, const void* scratch,
+                              void* dq, hipStream_t stream);
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
                                        void* dv, hipStream_t stream);
 

@@ -65,7 +65,21 @@ typedef struct msa_problem {
   int32_t max_doc_chunks;  /* max_d ceil(len_d / 8); <= MSA_MAX_DOC_CHUNKS */
   int32_t num_cus;         /* compute units the walk is sized for (msa_device_check) */
   float softmax_scale;     /* usually head_dim ** -0.5 (msa_schedule: SOFTMAX_SCALE) */
+  int32_t dq_mode;         /* MSA_DQ_RECOMPUTE (default) or MSA_DQ_ATOMIC_POOL */
 } msa_problem;
+
+/* How the backward forms dQ.
+ * MSA_DQ_ATOMIC_POOL: the main kernel scatters each tile's dQ with fp32
+ *   atomics into a [T, Hq, D] pool that the postprocess casts to bf16
+ *   (msa_backward_sm100 page: dQ^T per tile into an atomic pool).  On MI355X
+ *   fp32 global atomics execute beyond the L2 at about 0.32 G lane-ops per
+ *   microsecond, so this mode is bound by the atomic rate (about 1 G
+ *   lane-atomics per call on an 8K-token, 4x16-head, top-16 problem).
+ * MSA_DQ_RECOMPUTE: the main kernel computes dK/dV only; msa_backward_dq runs
+ *   a query-parallel kernel that recomputes S^T and dP^T per (chunk, block),
+ *   accumulates dQ in registers and writes bf16 dq once (no atomics). */
+#define MSA_DQ_RECOMPUTE 0
+#define MSA_DQ_ATOMIC_POOL 1
 
 #define MSA_MAX_DOC_CHUNKS (1 << 18) /* documents up to 2 Mi tokens (32 KiB LDS bitmap per bucket sort) */
 
@@ -122,27 +136,35 @@ int msa_forward(const msa_problem* p, const void* q, const void* k, const void* 
                 const int32_t* cu_seqlens, const int32_t* sched, void* out, float* lse,
                 void* stream);
 
-/* Bytes of fp32 scratch msa_backward needs: Delta [T, Hq], the dQ pool
- * [T, Hq, D] and dK, dV accumulators [T, Hkv, D]. */
+/* Bytes of fp32 scratch msa_backward needs: Delta [T, Hq], dK and dV
+ * accumulators [T, Hkv, D], and in MSA_DQ_ATOMIC_POOL mode the dQ pool
+ * [T, Hq, D]. */
 int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
 
 /* KV-parallel backward (msa_backward_sm100: run_backward): preprocess
  * (Delta = rowsum(dout * out), zero the accumulators), main kernel (per walk
- * of task rows: K/V resident per bucket, five bf16 MFMA contractions per
- * 128-row tile, dK/dV flushed per bucket segment with fp32 atomics, dQ
- * scattered with fp32 atomics into the pool), postprocess (cast to bf16).
+ * of task rows: K/V resident per bucket, bf16 MFMA contractions S^T, dP^T,
+ * dV, dK per 128-row tile, dK/dV flushed per bucket segment with fp32
+ * atomics; in MSA_DQ_ATOMIC_POOL mode also dQ^T per tile scattered into the
+ * pool), the dQ kernel (MSA_DQ_RECOMPUTE mode), postprocess (cast to bf16).
  * dk/dv rows that no query attends are exactly 0. */
 int msa_backward(const msa_problem* p, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
                  const int32_t* sched, void* scratch, void* dq, void* dk, void* dv, void* stream);
 
-/* The three steps of msa_backward, callable one at a time (same arguments
- * and scratch; used to time each kernel).  Must run in this order. */
+/* The steps of msa_backward, callable one at a time (same arguments and
+ * scratch; used to time each kernel).  Order: preprocess, main, dq,
+ * postprocess.  msa_backward_dq writes dq directly and does nothing in
+ * MSA_DQ_ATOMIC_POOL mode; msa_backward_postprocess writes dq only in that
+ * mode. */
 int msa_backward_preprocess(const msa_problem* p, const void* out, const void* dout,
                             void* scratch, void* stream);
 int msa_backward_main(const msa_problem* p, const void* q, const void* k, const void* v,
                       const void* dout, const float* lse, const int32_t* cu_seqlens,
                       const int32_t* sched, void* scratch, void* stream);
+int msa_backward_dq(const msa_problem* p, const void* q, const void* k, const void* v,
+                    const void* dout, const float* lse, const int32_t* cu_seqlens,
+                    const int32_t* sched, const void* scratch, void* dq, void* stream);
 int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk,
                              void* dv, void* stream);
 

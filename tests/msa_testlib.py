@@ -16,10 +16,10 @@ def device_cus() -> int:
     return B.msa_device_check(0)
 
 
-def problem_for(w, num_cus=None) -> B.Problem:
+def problem_for(w, num_cus=None, dq_mode=B.DQ_RECOMPUTE) -> B.Problem:
     return B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk,
                           num_cus=num_cus if num_cus is not None else device_cus(),
-                          softmax_scale=w.scale, block_size=w.block)
+                          softmax_scale=w.scale, block_size=w.block, dq_mode=dq_mode)
 
 
 def to_dev(w):

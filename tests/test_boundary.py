@@ -42,7 +42,10 @@ def test_schedule_layout_is_host_only_and_sized():
     offs = [L.desc, L.err, L.doc_chunk_off, L.doc_blk_off, L.chunk_doc, L.sel_clean, L.row_cursor,
             L.row_ptr, L.head_off, L.q_idx, L.task_meta, L.total]
     assert offs == sorted(offs)
-    assert B.msa_backward_scratch_bytes(p) >= 4 * 8192 * 64 * (1 + 128) + 2 * 4 * 8192 * 4 * 128
+    base = 4 * 8192 * 64 + 2 * 4 * 8192 * 4 * 128            # Delta, dK, dV (fp32)
+    assert base <= B.msa_backward_scratch_bytes(p) < base + 4096
+    pa = B.Problem(**{**p.__dict__, "dq_mode": B.DQ_ATOMIC_POOL})
+    assert B.msa_backward_scratch_bytes(pa) >= base + 4 * 8192 * 64 * 128   # plus the fp32 dQ pool
 
 
 @pytest.mark.parametrize("field,value,exc", [
@@ -53,6 +56,7 @@ def test_schedule_layout_is_host_only_and_sized():
     ("num_chunks", 5, ValueError),
     ("num_docs", 0, ValueError),
     ("softmax_scale", 0.0, ValueError),
+    ("dq_mode", 2, ValueError),
 ])
 def test_bad_problems_are_rejected_on_the_host(field, value, exc):
     good = B.Problem.make([0, 512], 1, 64, 4)

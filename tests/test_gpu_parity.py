@@ -71,12 +71,13 @@ SMALL["empty_chunks"] = _empty_rows_workload
 
 
 @pytest.mark.parametrize("case", list(SMALL))
-@pytest.mark.parametrize("num_cus", [None, 7])
-def test_small_cases_full_parity(case, num_cus):
+@pytest.mark.parametrize("num_cus,dq_mode", [(None, B.DQ_RECOMPUTE), (7, B.DQ_RECOMPUTE),
+                                             (None, B.DQ_ATOMIC_POOL), (7, B.DQ_ATOMIC_POOL)])
+def test_small_cases_full_parity(case, num_cus, dq_mode):
     w = SMALL[case]()
-    print(f"[case] {case} num_cus={num_cus} T={w.total_tokens} Hkv={w.num_kv_heads} "
-          f"D={w.head_dim} k={w.topk}", flush=True)
-    p = TL.problem_for(w, num_cus)
+    print(f"[case] {case} num_cus={num_cus} dq_mode={dq_mode} T={w.total_tokens} "
+          f"Hkv={w.num_kv_heads} D={w.head_dim} k={w.topk}", flush=True)
+    p = TL.problem_for(w, num_cus, dq_mode)
     t = TL.to_dev(w)
     sched = TL.run_schedule(w, p, t)
     want = TL.compare_schedule(w, p, sched)
@@ -100,11 +101,12 @@ def test_small_cases_full_parity(case, num_cus):
 FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_configs_sampled(name):
-    print(f"[case] full-size {name}", flush=True)
+@pytest.mark.parametrize("name,dq_mode", [(n, B.DQ_RECOMPUTE) for n in FULL] +
+                         [("single8k", B.DQ_ATOMIC_POOL)])
+def test_full_size_configs_sampled(name, dq_mode):
+    print(f"[case] full-size {name} dq_mode={dq_mode}", flush=True)
     w = make_workload(name)
-    p = TL.problem_for(w)
+    p = TL.problem_for(w, dq_mode=dq_mode)
     t = TL.to_dev(w)
     sched = TL.run_schedule(w, p, t)
     want = TL.compare_schedule(w, p, sched)
