@@ -298,10 +298,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     }
     const float l2 = sm.lse2[mq];
     const float dl = sm.delta[mq];
-    // Keys of this block at tile offset <= klim are visible to this query
-    // (causal within the diagonal block, and inside the document).
-    const int pq = qb + (mq >> 4);
-    const int klim = min(pq, len - 1) - b * kBlock;
+    // Only the diagonal block holds keys after a query (or past the document
+    // end): there, keys at block offset > klim get score -inf, so P = 0.
+    if ((b + 1) * kBlock - 1 > qb) {
+      const int pq = qb + (mq >> 4);
+      const int klim = min(pq, len - 1) - b * kBlock;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
+          st[t][j] = key <= klim ? st[t][j] : -INFINITY;
+        }
+    }
     bf16x8 dsa[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -311,9 +320,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int j = 4 * jg + rr;
-          const int key = 32 * t + 8 * jg + 4 * h + rr;
-          float pv = fast_exp2(st[t][j] * c2 - l2);
-          pv = key <= klim ? pv : 0.f;
+          const float pv = fast_exp2(fmaf(st[t][j], c2, -l2));
           const float dsv = pv * (dpt[t][j] - dl);
           p4[rr] = (bf16)pv;
           d4[rr] = (bf16)dsv;

@@ -155,15 +155,24 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
     }
 
     // dS^T in bf16, packed as B operands of dQ^T (k step u = keys 16u..16u+15).
-    const int klim = min(pq, len - 1) - b * kBlock;
+    // Only the diagonal block holds keys after a query (or past the document
+    // end); there those scores become -inf, so P = 0.
+    if ((b + 1) * kBlock - 1 > p0) {
+      const int klim = min(pq, len - 1) - b * kBlock;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
+          st[t][j] = key <= klim ? st[t][j] : -INFINITY;
+        }
+    }
     bf16x8 dsb[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
-        float pv_ = fast_exp2(st[t][j] * c2 - l2);
-        pv_ = key <= klim ? pv_ : 0.f;
+        const float pv_ = fast_exp2(fmaf(st[t][j], c2, -l2));
         dsb[2 * t + (j >> 3)][j & 7] = (bf16)(pv_ * (dpt[t][j] - dl));
       }
     }

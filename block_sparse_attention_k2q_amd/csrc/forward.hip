@@ -5,18 +5,20 @@
 // forward's bf16 out [T, Hq, D] and fp32 lse [T, Hq]).  The kernel below is
 // this library's own design for CDNA4:
 //
-//  * one workgroup per (chunk, index head): a 128-row query tile of 8 tokens
-//    x 16 query heads that share one KV head; workgroup ids run head-fastest
-//    so that, with 4 or 8 KV heads, each XCD (ids are dealt to the 8 XCDs
-//    round-robin) only ever reads the K/V of one head;
-//  * 4 waves, each owning 32 query rows (2 tokens x 16 heads); the tile's Q
-//    rows live in registers as MFMA B operands for the whole chunk;
-//  * per kept key block (64 keys): K and V are staged in LDS (next block
-//    prefetched into registers while the current one is consumed),
-//    S^T = K Q^T (keys x queries) so that every lane owns one query column,
-//    online softmax in the exp2 domain with the causal mask on the diagonal
-//    block, and O^T += V^T P^T with P^T taken straight from the S^T
-//    accumulators (V^T read with the LDS transpose load);
+//  * one workgroup of 2 waves per (chunk, index head): a 128-row query tile
+//    of 8 tokens x 16 query heads sharing one KV head, each wave owning 64
+//    rows (two 32-query MFMA columns).  Workgroup ids run head-fastest, so
+//    with 4 or 8 KV heads each XCD (ids are dealt to the 8 XCDs round-robin)
+//    reads the K/V of one head only, which then stays in its L2;
+//  * the tile's Q rows live in registers as MFMA B operands for the whole
+//    chunk;
+//  * per kept key block (64 keys): K and V arrive in LDS by direct
+//    global->LDS loads into one of two swizzled buffers, the next block's
+//    copy in flight while the current one is consumed (one barrier per
+//    block);  S^T = K Q^T (keys x queries, so a lane owns one query column),
+//    online softmax in the exp2 domain with the causal mask, and
+//    O^T += V^T P^T with P^T taken straight from the S^T accumulators and V^T
+//    read by the LDS transpose load;
 //  * out = O / l in bf16, lse = ln(sum exp(scale * s)) in fp32.
 #include "msa_device.h"
 #include "msa_internal.h"
@@ -25,32 +27,62 @@ namespace msa {
 
 namespace {
 
-constexpr int kFwdThreads = 256;
+constexpr float kRescaleLog2 = 8.f;
+#ifndef MSA_FWD_NQ
+#define MSA_FWD_NQ 1
+#endif
+constexpr int kFwdNQ = MSA_FWD_NQ;
 
 template <int D>
-struct FwdSmem {
-  static constexpr int LDK = D + 8;    // padded row pitch of the K tile (bf16 elements)
-  static constexpr int LDV = D + 16;   // padded row pitch of the V tile
-  bf16 k[kBlock * LDK];
-  bf16 v[kBlock * LDV];
-  int blocks[64];
-  int nblocks;
+struct FwdTiles {
+  bf16 k[kBlock * D];
+  bf16 v[kBlock * D];
 };
 
-template <int D>
-__global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
+// Copy key block b (K and V rows of KV head i) into a swizzled tile pair.
+// Keys past the document end read the document's last key instead: they are
+// masked out of the softmax, and their values are finite.
+// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
+// 64 / CPR rows); lane l supplies physical chunk l of its piece.
+template <int D, int NWAVES>
+__device__ __forceinline__ void stage_kv(FwdTiles<D>& t, const bf16* __restrict__ k,
+                                         const bf16* __restrict__ v, int tok0, int len, int b, int Hkv,
+                                         int i, int w, int lane) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPP = 64 / CPR;              // rows per piece
+  constexpr int PIECES = kBlock / RPP;       // pieces per tensor
+  const int64_t row_stride = (int64_t)Hkv * D;
+  const bf16* kbase = k + ((int64_t)tok0 * Hkv + i) * D;
+  const bf16* vbase = v + ((int64_t)tok0 * Hkv + i) * D;
+  const int lrow = lane / CPR, pcol = lane % CPR;
+  const int kmax = len - 1 - b * kBlock;     // last valid key offset in this block
+#pragma unroll
+  for (int n = 0; n < PIECES / NWAVES; ++n) {
+    const int piece = n * NWAVES + w;
+    const int row = piece * RPP + lrow;
+    const int lc = pcol ^ chunk_swizzle<CPR>(row);
+    const int64_t off = (int64_t)(b * kBlock + min(row, kmax)) * row_stride + 8 * lc;
+    dma16(kbase + off, t.k + piece * 512);
+    dma16(vbase + off, t.v + piece * 512);
+  }
+}
+
+// NQ = 32-query MFMA columns per wave; the 128-row tile takes 4 / NQ waves.
+template <int D, int NQ>
+__global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
     const int32_t* __restrict__ err, bf16* __restrict__ out, float* __restrict__ lse, int Hkv, int C,
     int K, float scale) {
-  using S = FwdSmem<D>;
-  constexpr int LDK = S::LDK, LDV = S::LDV;
+  constexpr int CPR = D / 8;
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
   constexpr int NT = D / 32;           // 32-wide d tiles of O^T
-  constexpr int VEC = D / 8;           // 16-byte vectors per K/V row
-  constexpr int PF = kBlock * VEC / kFwdThreads;  // prefetch vectors per thread per tensor
-  __shared__ __attribute__((aligned(16))) S sm;
+  constexpr int NW = 4 / NQ;            // waves per workgroup
+  __shared__ __attribute__((aligned(16))) FwdTiles<D> buf0;
+  __shared__ __attribute__((aligned(16))) FwdTiles<D> buf1;
+  __shared__ int s_blocks[64];
+  __shared__ int s_nblocks;
 
   if (err[1]) return;
   const int i = blockIdx.x % Hkv;
@@ -68,143 +100,170 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const int32_t* row = sel_clean + ((int64_t)i * C + g) * K;
     for (int s = 0; s < K; ++s) {
       const int b = row[s];
-      if (b >= 0) sm.blocks[n++] = b;
+      if (b >= 0) s_blocks[n++] = b;
     }
-    sm.nblocks = n;
+    s_nblocks = n;
   }
 
   const int w = wave_id(), lane = lane_id();
   const int n32 = lane & 31, h = lane >> 5;
-  const int jq = 2 * w + (n32 >> 4);         // token of this lane's query column
-  const int hh = n32 & 15;
-  const bool qvalid = jq < qcount;
-  const int pq = p0 + jq;                    // document-local query position
-  const int64_t qrow = (int64_t)(tok0 + p0 + jq) * Hq + kQPerKV * i + hh;
-
-  bf16x8 qf[KS];
+  // Query column nq of this lane: tile row 32(NQ w + nq) + n32, i.e. token
+  // 2(NQ w + nq) + n32/16 and head n32%16.
+  int jq[NQ], pq[NQ];
+  bool qvalid[NQ];
+  int64_t qrow[NQ];
+  bf16x8 qf[NQ][KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (qvalid) qf[s] = load_bf16x8(q + qrow * D + 16 * s + 8 * h);
-    else qf[s] = bf16x8{};
+  for (int nq = 0; nq < NQ; ++nq) {
+    jq[nq] = 2 * (NQ * w + nq) + (n32 >> 4);
+    qvalid[nq] = jq[nq] < qcount;
+    pq[nq] = p0 + jq[nq];
+    qrow[nq] = (int64_t)(tok0 + p0 + min(jq[nq], qcount - 1)) * Hq + kQPerKV * i + (n32 & 15);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[nq][s] = qvalid[nq] ? load_bf16x8(q + qrow[nq] * D + 16 * s + 8 * h) : bf16x8{};
   }
 
-  floatx16 o[NT];
+  floatx16 o[NT][NQ];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = floatx16{};
-  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) o[t][nq] = floatx16{};
+  float m[NQ], l[NQ];
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) { m[nq] = -INFINITY; l[nq] = 0.f; }
   const float c2 = scale * kLog2e;
 
   lds_barrier();
-  const int nblk = sm.nblocks;
+  const int nblk = s_nblocks;
+  if (nblk > 0) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[0], Hkv, i, w, lane);
 
-  // Register prefetch of one block's K and V rows (zero past the document end).
-  u32x4 pk[PF], pv[PF];
-  auto prefetch = [&](int b) {
+  auto consume = [&](const FwdTiles<D>& t, int b) {
+    // S^T = K Q^T: two 32-key tiles x two query columns; operands of k step
+    // s+1 are read while step s runs.
+    floatx16 st[2][NQ];
 #pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int e = threadIdx.x + x * kFwdThreads;
-      const int row = e / VEC, col = (e % VEC) * 8;
-      const int key = b * kBlock + row;
-      if (key < len) {
-        const int64_t off = ((int64_t)(tok0 + key) * Hkv + i) * D + col;
-        pk[x] = *reinterpret_cast<const u32x4*>(k + off);
-        pv[x] = *reinterpret_cast<const u32x4*>(v + off);
-      } else {
-        pk[x] = u32x4{0, 0, 0, 0};
-        pv[x] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  if (nblk > 0) prefetch(sm.blocks[0]);
-
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int b = sm.blocks[bi];
-    lds_barrier();  // all waves are done with the previous block's tiles
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int e = threadIdx.x + x * kFwdThreads;
-      const int row = e / VEC, col = (e % VEC) * 8;
-      *reinterpret_cast<u32x4*>(&sm.k[row * LDK + col]) = pk[x];
-      *reinterpret_cast<u32x4*>(&sm.v[row * LDV + col]) = pv[x];
-    }
-    lds_barrier();
-    if (bi + 1 < nblk) prefetch(sm.blocks[bi + 1]);
-
-    // S^T = K Q^T: two 32-key tiles.
-    floatx16 st[2] = {floatx16{}, floatx16{}};
+      for (int nq = 0; nq < NQ; ++nq) st[a][nq] = floatx16{};
+    bf16x8 ak[2][2];
+    ak[0][0] = lds_row8<CPR>(t.k, n32, 8 * h);
+    ak[0][1] = lds_row8<CPR>(t.k, 32 + n32, 8 * h);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 a = load_bf16x8(&sm.k[(32 * t + n32) * LDK + 16 * s + 8 * h]);
-        st[t] = mfma32(a, qf[s], st[t]);
+      if (s + 1 < KS) {
+        ak[(s + 1) & 1][0] = lds_row8<CPR>(t.k, n32, 16 * (s + 1) + 8 * h);
+        ak[(s + 1) & 1][1] = lds_row8<CPR>(t.k, 32 + n32, 16 * (s + 1) + 8 * h);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) st[a][nq] = mfma32(ak[s & 1][a], qf[nq][s], st[a][nq]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Scores in the log2 domain; causal mask only where the block can hold
-    // keys after this query (the diagonal block).
-    const bool need_mask = (b + 1) * kBlock - 1 > p0;
-    float mx = -INFINITY;
+    // Online softmax per query column.  Only the diagonal block holds keys
+    // after a query (or past the document end): there, keys at block offset
+    // > klim are set to -inf before the max.
+    const bool diag = (b + 1) * kBlock - 1 > p0;
+    bf16x8 pb[NQ][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int nq = 0; nq < NQ; ++nq) {
+      if (diag) {
+        const int klim = min(pq[nq], len - 1) - b * kBlock;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = st[t][j] * c2;
-        if (need_mask) {
-          const int key = b * kBlock + 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
-          if (key > pq || key >= len) x = -INFINITY;
-        }
-        st[t][j] = x;
-        mx = fmaxf(mx, x);
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = 32 * a + 8 * (j >> 2) + 4 * h + (j & 3);
+            st[a][nq][j] = key <= klim ? st[a][nq][j] : -INFINITY;
+          }
       }
-    }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
-    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
-    float psum = 0.f;
-    bf16x8 pb[4];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float pv_ = fast_exp2(st[t][j] - msub);
-        psum += pv_;
-        pb[2 * t + (j >> 3)][j & 7] = (bf16)pv_;
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[a][nq][j]);
+      mx = fmaxf(mx, swap_halves(mx)) * c2;   // max in the scaled log2 domain
+      // Lazy rescale: the running max m only moves when a score exceeds it by
+      // more than kRescaleLog2, so P = exp2(s - m) stays <= 2^kRescaleLog2 and
+      // the O accumulators are rescaled only on the (rare) blocks that move it.
+      const bool move = mx > m[nq] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? mx : m[nq];
+        const float alpha = (m[nq] == -INFINITY) ? 0.f : fast_exp2(m[nq] - m_new);
+        l[nq] *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) o[tt][nq] *= alpha;
+        m[nq] = m_new;
       }
-    }
-    l = l * alpha + psum;
-    m = m_new;
+      const float msub = (m[nq] == -INFINITY) ? 0.f : m[nq];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] *= alpha;
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          pb[nq][2 * a + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(st[a][nq][j], c2, -msub));
+      // Row sum of the bf16 probabilities that enter O (same values normalise it).
+#pragma unroll
+      for (int u = 0; u < 4; ++u) l[nq] = sum_bf16x8(pb[nq][u], l[nq]);
+    }
 
-    // O^T += V^T P^T over the 4 k steps of 16 keys.
+    // O^T += V^T P^T over 4 k steps of 16 keys; V^T operands double-buffered.
+    bf16x8 av[2][NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      av[0][tt] = lds_tr_operand_swz<CPR>(t.v, 32 * tt, lane, 0, 4, 8, 12);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      if (u + 1 < 4) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 a = lds_tr_operand(sm.v, LDV, 32 * t, lane, 16 * u, 16 * u + 4, 16 * u + 8,
-                                        16 * u + 12);
-        o[t] = mfma32(a, pb[u], o[t]);
+        for (int tt = 0; tt < NT; ++tt)
+          av[(u + 1) & 1][tt] = lds_tr_operand_swz<CPR>(t.v, 32 * tt, lane, 16 * (u + 1),
+                                                        16 * (u + 1) + 4, 16 * (u + 1) + 8,
+                                                        16 * (u + 1) + 12);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) o[tt][nq] = mfma32(av[u & 1][tt], pb[nq][u], o[tt][nq]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int bi = 0; bi < nblk; bi += 2) {
+    // Even blocks use buf0, odd blocks buf1.
+    wait_vmem();
+    lds_barrier();   // block bi landed in buf0; all waves are done with buf1
+    if (bi + 1 < nblk) stage_kv<D, NW>(buf1, k, v, tok0, len, s_blocks[bi + 1], Hkv, i, w, lane);
+    consume(buf0, s_blocks[bi]);
+    if (bi + 1 < nblk) {
+      wait_vmem();
+      lds_barrier();  // block bi+1 landed in buf1; all waves are done with buf0
+      if (bi + 2 < nblk) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[bi + 2], Hkv, i, w, lane);
+      consume(buf1, s_blocks[bi + 1]);
     }
   }
 
-  const float l_tot = l + swap_halves(l);
-  if (!qvalid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  bf16* orow = out + qrow * D;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int nq = 0; nq < NQ; ++nq) {
+    const float l_tot = l[nq] + swap_halves(l[nq]);
+    if (!qvalid[nq]) continue;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* orow = out + qrow[nq] * D;
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) {
-      bf16x4 v4;
+    for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v4[r] = (bf16)(o[t][4 * jg + r] * inv);
-      store_bf16x4(orow + 32 * t + 8 * jg + 4 * h, v4);
+      for (int jg = 0; jg < 4; ++jg) {
+        bf16x4 v4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = (bf16)(o[tt][nq][4 * jg + r] * inv);
+        store_bf16x4(orow + 32 * tt + 8 * jg + 4 * h, v4);
+      }
     }
+    if (h == 0) lse[qrow[nq]] = l_tot > 0.f ? (m[nq] + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
-  if (h == 0) lse[qrow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -214,14 +273,14 @@ hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, co
                           void* out, float* lse, hipStream_t stream) {
   const int64_t nwg = (int64_t)p.num_chunks * p.num_kv_heads;
   if (nwg == 0) return hipSuccess;
-  auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kFwdThreads), 0, stream, (const bf16*)q,
+  auto args = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(threads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, cu, sched + L.chunk_doc, sched + L.doc_chunk_off,
                        sched + L.sel_clean, sched + L.err, (bf16*)out, lse, p.num_kv_heads,
                        p.num_chunks, p.topk, p.softmax_scale);
   };
-  if (p.head_dim == 128) args(forward_kernel<128>);
-  else args(forward_kernel<64>);
+  if (p.head_dim == 128) args(forward_kernel<128, kFwdNQ>, 256 / kFwdNQ);
+  else args(forward_kernel<64, kFwdNQ>, 256 / kFwdNQ);
   return hipGetLastError();
 }
 

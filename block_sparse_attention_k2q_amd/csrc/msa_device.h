@@ -77,7 +77,62 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* base, int ld, int c
   return join_tr(lo, hi);
 }
 
+__device__ __forceinline__ bf16x8 load_bf16x8_lds(const bf16* p);
+
+// ---------------------------------------------------------------------------
+// Unpadded row-major bf16 tiles whose 16-byte chunks are XOR-swizzled per row
+// (D = 8 * CPR elements per row).  The swizzle keeps both access patterns of
+// the kernels free of LDS bank conflicts on a 64-bank LDS:
+//  * 16 consecutive rows read at one logical chunk (MFMA row operands), and
+//  * 4 consecutive rows read across 4 consecutive chunks (transpose loads).
+// ---------------------------------------------------------------------------
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  static_assert(CPR == 16 || CPR == 8, "rows of 128 or 64 bf16");
+  if constexpr (CPR == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Element offset of (row, col) in a swizzled tile with CPR chunks per row.
+template <int CPR>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * (8 * CPR) + ((((col >> 3) ^ chunk_swizzle<CPR>(row))) << 3) + (col & 7);
+}
+
+// MFMA row operand: 8 consecutive bf16 of `row` starting at col (col % 8 == 0).
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_row8(const bf16* tile, int row, int col) {
+  return load_bf16x8_lds(tile + swz_off<CPR>(row, col));
+}
+
+// Transposing operand from a swizzled tile (same contract as lds_tr_operand).
+template <int CPR>
+__device__ __forceinline__ bf16x8 lds_tr_operand_swz(const bf16* tile, int col0, int lane, int row_lo_h0,
+                                                     int row_lo_h1, int row_hi_h0, int row_hi_h1) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+  const int h = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * c;
+  const int rlo = (h ? row_lo_h1 : row_lo_h0) + r;
+  const int rhi = (h ? row_hi_h1 : row_hi_h0) + r;
+  shortx4 lo = lds_read_tr4(tile + swz_off<CPR>(rlo, col));
+  shortx4 hi = lds_read_tr4(tile + swz_off<CPR>(rhi, col));
+  return join_tr(lo, hi);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after lds_wave_base (wave-uniform).
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
+                                   0);
+}
+
+// Wait until this wave has no outstanding vector-memory operations.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 load_bf16x8_lds(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void store_bf16x8(bf16* p, bf16x8 v) {
@@ -98,6 +153,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// acc + sum of the 8 bf16 values of v (dot products with (1, 1) on bf16 pairs).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16x2 pr = {v[2 * e], v[2 * e + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
 }
 
 // Value held by lane (l ^ 32).
