@@ -100,6 +100,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dq-mode", choices=("recompute", "atomic"), default="recompute")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device-to-device copy of this many MiB "
+                         "three times (the known-size reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU "
@@ -202,6 +205,14 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(tflops[dominant] / PEAK_BF16_TFLOPS, 4),
                      "kernel": KERNEL_NAMES[dominant], "traffic": measured_traffic(dominant)},
     }
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = nbytes
     if not args.no_cpu_baseline:
         from oracle import msa_oracle as O
         sched_host = O.build_schedule(w.sel, w.cu_seqlens, w.block, num_cus)
