@@ -10,8 +10,9 @@
 //
 //  * one workgroup per (chunk, index head), 4 waves x 32 query rows; Q and
 //    dO rows of the tile stay in registers as MFMA B operands;
-//  * per kept block: K and V staged in LDS (next block prefetched into
-//    registers), S^T = K Q^T and dP^T = V dO^T (keys x queries),
+//  * per kept block: K and V arrive in one of two swizzled LDS buffers by
+//    direct global->LDS loads (next block in flight while the current one is
+//    consumed), S^T = K Q^T and dP^T = V dO^T (keys x queries),
 //    P^T = exp2(S^T * scale * log2e - LSE * log2e) with the causal mask,
 //    dS^T = P^T (dP^T - Delta), and dQ^T += K^T dS^T with dS^T taken straight
 //    from the accumulators and K^T read through the LDS transpose load;
@@ -26,28 +27,20 @@ namespace {
 constexpr int kDqThreads = 256;
 
 template <int D>
-struct DqSmem {
-  static constexpr int LDK = D + 8;
-  bf16 k[kBlock * LDK];
-  bf16 v[kBlock * LDK];
-  int blocks[64];
-  int nblocks;
-};
-
-template <int D>
-__global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
+__global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
     const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv, int C, int K, float scale) {
-  using S = DqSmem<D>;
-  constexpr int LDK = S::LDK;
+  constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
-  constexpr int VEC = D / 8;
-  constexpr int PF = kBlock * VEC / kDqThreads;
-  __shared__ __attribute__((aligned(16))) S sm;
+  constexpr int NW = kDqThreads / 64;
+  __shared__ __attribute__((aligned(16))) KVTiles<D> buf0;
+  __shared__ __attribute__((aligned(16))) KVTiles<D> buf1;
+  __shared__ int s_blocks[64];
+  __shared__ int s_nblocks;
 
   if (err[1]) return;
   const int i = blockIdx.x % Hkv;
@@ -65,9 +58,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
     const int32_t* row = sel_clean + ((int64_t)i * C + g) * K;
     for (int s = 0; s < K; ++s) {
       const int b = row[s];
-      if (b >= 0) sm.blocks[n++] = b;
+      if (b >= 0) s_blocks[n++] = b;
     }
-    sm.nblocks = n;
+    s_nblocks = n;
   }
 
   const int w = wave_id(), lane = lane_id();
@@ -94,64 +87,35 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
   for (int t = 0; t < NT; ++t) acc[t] = floatx16{};
 
   lds_barrier();
-  const int nblk = sm.nblocks;
+  const int nblk = s_nblocks;
+  if (nblk > 0) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[0], Hkv, i, w, lane);
 
-  u32x4 pk[PF], pv[PF];
-  auto prefetch = [&](int b) {
-#pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int e = threadIdx.x + x * kDqThreads;
-      const int row = e / VEC, col = (e % VEC) * 8;
-      const int key = b * kBlock + row;
-      if (key < len) {
-        const int64_t off = ((int64_t)(tok0 + key) * Hkv + i) * D + col;
-        pk[x] = *reinterpret_cast<const u32x4*>(k + off);
-        pv[x] = *reinterpret_cast<const u32x4*>(v + off);
-      } else {
-        pk[x] = u32x4{0, 0, 0, 0};
-        pv[x] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  if (nblk > 0) prefetch(sm.blocks[0]);
-
-  for (int bi = 0; bi < nblk; ++bi) {
-    const int b = sm.blocks[bi];
-    lds_barrier();
-#pragma unroll
-    for (int x = 0; x < PF; ++x) {
-      const int e = threadIdx.x + x * kDqThreads;
-      const int row = e / VEC, col = (e % VEC) * 8;
-      *reinterpret_cast<u32x4*>(&sm.k[row * LDK + col]) = pk[x];
-      *reinterpret_cast<u32x4*>(&sm.v[row * LDK + col]) = pv[x];
-    }
-    lds_barrier();
-    if (bi + 1 < nblk) prefetch(sm.blocks[bi + 1]);
-
+  auto consume = [&](const KVTiles<D>& t, int b) {
     // S^T = K Q^T and dP^T = V dO^T, operands of step s+1 read during step s.
     floatx16 st[2] = {floatx16{}, floatx16{}};
     floatx16 dpt[2] = {floatx16{}, floatx16{}};
-    {
-      bf16x8 ak[2][2], av[2][2];
-      auto load_step = [&](int s, int slot) {
+    bf16x8 ak[2][2], av[2][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          ak[slot][t] = load_bf16x8(&sm.k[(32 * t + n32) * LDK + 16 * s + 8 * h]);
-          av[slot][t] = load_bf16x8(&sm.v[(32 * t + n32) * LDK + 16 * s + 8 * h]);
+    for (int a = 0; a < 2; ++a) {
+      ak[0][a] = lds_row8<CPR>(t.k, 32 * a + n32, 8 * h);
+      av[0][a] = lds_row8<CPR>(t.v, 32 * a + n32, 8 * h);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          ak[(s + 1) & 1][a] = lds_row8<CPR>(t.k, 32 * a + n32, 16 * (s + 1) + 8 * h);
+          av[(s + 1) & 1][a] = lds_row8<CPR>(t.v, 32 * a + n32, 16 * (s + 1) + 8 * h);
         }
-      };
-      load_step(0, 0);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) load_step(s + 1, (s + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          st[t] = mfma32(ak[s & 1][t], qf[s], st[t]);
-          dpt[t] = mfma32(av[s & 1][t], of[s], dpt[t]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        st[a] = mfma32(ak[s & 1][a], qf[s], st[a]);
+        dpt[a] = mfma32(av[s & 1][a], of[s], dpt[a]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // dS^T in bf16, packed as B operands of dQ^T (k step u = keys 16u..16u+15).
@@ -160,41 +124,52 @@ __global__ __launch_bounds__(kDqThreads, 1) void dq_kernel(
     if ((b + 1) * kBlock - 1 > p0) {
       const int klim = min(pq, len - 1) - b * kBlock;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int key = 32 * t + 8 * (j >> 2) + 4 * h + (j & 3);
-          st[t][j] = key <= klim ? st[t][j] : -INFINITY;
+          const int key = 32 * a + 8 * (j >> 2) + 4 * h + (j & 3);
+          st[a][j] = key <= klim ? st[a][j] : -INFINITY;
         }
     }
     bf16x8 dsb[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float pv_ = fast_exp2(fmaf(st[t][j], c2, -l2));
-        dsb[2 * t + (j >> 3)][j & 7] = (bf16)(pv_ * (dpt[t][j] - dl));
+        const float pv = fast_exp2(fmaf(st[a][j], c2, -l2));
+        dsb[2 * a + (j >> 3)][j & 7] = (bf16)(pv * (dpt[a][j] - dl));
       }
-    }
 
-    // dQ^T += K^T dS^T.
-    {
-      bf16x8 ak[2][NT];
-      auto load_u = [&](int u, int slot) {
+    // dQ^T += K^T dS^T, K^T operands double-buffered.
+    bf16x8 kt[2][NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          ak[slot][t] = lds_tr_operand(sm.k, LDK, 32 * t, lane, 16 * u, 16 * u + 4, 16 * u + 8,
-                                       16 * u + 12);
-      };
-      load_u(0, 0);
+    for (int tt = 0; tt < NT; ++tt) kt[0][tt] = lds_tr_operand_swz<CPR>(t.k, 32 * tt, lane, 0, 4, 8, 12);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u + 1 < 4) load_u(u + 1, (u + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < 4; ++u) {
+      if (u + 1 < 4) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma32(ak[u & 1][t], dsb[u], acc[t]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int tt = 0; tt < NT; ++tt)
+          kt[(u + 1) & 1][tt] = lds_tr_operand_swz<CPR>(t.k, 32 * tt, lane, 16 * (u + 1), 16 * (u + 1) + 4,
+                                                        16 * (u + 1) + 8, 16 * (u + 1) + 12);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma32(kt[u & 1][tt], dsb[u], acc[tt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int bi = 0; bi < nblk; bi += 2) {
+    // Even blocks use buf0, odd blocks buf1.
+    wait_vmem();
+    lds_barrier();   // block bi landed in buf0; all waves are done with buf1
+    if (bi + 1 < nblk) stage_kv<D, NW>(buf1, k, v, tok0, len, s_blocks[bi + 1], Hkv, i, w, lane);
+    consume(buf0, s_blocks[bi]);
+    if (bi + 1 < nblk) {
+      wait_vmem();
+      lds_barrier();  // block bi+1 landed in buf1; all waves are done with buf0
+      if (bi + 2 < nblk) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[bi + 2], Hkv, i, w, lane);
+      consume(buf1, s_blocks[bi + 1]);
     }
   }
 

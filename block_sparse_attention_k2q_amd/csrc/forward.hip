@@ -28,44 +28,10 @@ namespace msa {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;
-#ifndef MSA_FWD_NQ
-#define MSA_FWD_NQ 1
-#endif
-constexpr int kFwdNQ = MSA_FWD_NQ;
-
-template <int D>
-struct FwdTiles {
-  bf16 k[kBlock * D];
-  bf16 v[kBlock * D];
-};
-
-// Copy key block b (K and V rows of KV head i) into a swizzled tile pair.
-// Keys past the document end read the document's last key instead: they are
-// masked out of the softmax, and their values are finite.
-// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
-// 64 / CPR rows); lane l supplies physical chunk l of its piece.
-template <int D, int NWAVES>
-__device__ __forceinline__ void stage_kv(FwdTiles<D>& t, const bf16* __restrict__ k,
-                                         const bf16* __restrict__ v, int tok0, int len, int b, int Hkv,
-                                         int i, int w, int lane) {
-  constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int RPP = 64 / CPR;              // rows per piece
-  constexpr int PIECES = kBlock / RPP;       // pieces per tensor
-  const int64_t row_stride = (int64_t)Hkv * D;
-  const bf16* kbase = k + ((int64_t)tok0 * Hkv + i) * D;
-  const bf16* vbase = v + ((int64_t)tok0 * Hkv + i) * D;
-  const int lrow = lane / CPR, pcol = lane % CPR;
-  const int kmax = len - 1 - b * kBlock;     // last valid key offset in this block
-#pragma unroll
-  for (int n = 0; n < PIECES / NWAVES; ++n) {
-    const int piece = n * NWAVES + w;
-    const int row = piece * RPP + lrow;
-    const int lc = pcol ^ chunk_swizzle<CPR>(row);
-    const int64_t off = (int64_t)(b * kBlock + min(row, kmax)) * row_stride + 8 * lc;
-    dma16(kbase + off, t.k + piece * 512);
-    dma16(vbase + off, t.v + piece * 512);
-  }
-}
+// One 32-query column per wave (4 waves per tile) fits 256 registers, so two
+// waves share each SIMD; two columns per wave halve the LDS reads but need
+// ~300 registers (one wave per SIMD) and measured slower.
+constexpr int kFwdNQ = 1;
 
 // NQ = 32-query MFMA columns per wave; the 128-row tile takes 4 / NQ waves.
 template <int D, int NQ>
@@ -79,8 +45,8 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
   constexpr int NT = D / 32;           // 32-wide d tiles of O^T
   constexpr int NW = 4 / NQ;            // waves per workgroup
-  __shared__ __attribute__((aligned(16))) FwdTiles<D> buf0;
-  __shared__ __attribute__((aligned(16))) FwdTiles<D> buf1;
+  __shared__ __attribute__((aligned(16))) KVTiles<D> buf0;
+  __shared__ __attribute__((aligned(16))) KVTiles<D> buf1;
   __shared__ int s_blocks[64];
   __shared__ int s_nblocks;
 
@@ -138,7 +104,7 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
   const int nblk = s_nblocks;
   if (nblk > 0) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[0], Hkv, i, w, lane);
 
-  auto consume = [&](const FwdTiles<D>& t, int b) {
+  auto consume = [&](const KVTiles<D>& t, int b) {
     // S^T = K Q^T: two 32-key tiles x two query columns; operands of k step
     // s+1 are read while step s runs.
     floatx16 st[2][NQ];

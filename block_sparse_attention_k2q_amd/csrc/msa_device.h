@@ -155,6 +155,42 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// K and V rows of one key block in LDS, each an unpadded swizzled tile.
+template <int D>
+struct KVTiles {
+  bf16 k[kBlock * D];
+  bf16 v[kBlock * D];
+};
+
+// Copy key block b (K and V rows of KV head i) into a swizzled tile pair.
+// Keys past the document end read the document's last key instead: they are
+// masked out of the softmax, and their values are finite.
+// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
+// 64 / CPR rows); lane l supplies physical chunk l of its piece.
+template <int D, int NWAVES>
+__device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__ k,
+                                         const bf16* __restrict__ v, int tok0, int len, int b, int Hkv,
+                                         int i, int w, int lane) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPP = 64 / CPR;              // rows per piece
+  constexpr int PIECES = kBlock / RPP;       // pieces per tensor
+  const int64_t row_stride = (int64_t)Hkv * D;
+  const bf16* kbase = k + ((int64_t)tok0 * Hkv + i) * D;
+  const bf16* vbase = v + ((int64_t)tok0 * Hkv + i) * D;
+  const int lrow = lane / CPR, pcol = lane % CPR;
+  const int kmax = len - 1 - b * kBlock;     // last valid key offset in this block
+#pragma unroll
+  for (int n = 0; n < PIECES / NWAVES; ++n) {
+    const int piece = n * NWAVES + w;
+    const int row = piece * RPP + lrow;
+    const int lc = pcol ^ chunk_swizzle<CPR>(row);
+    const int64_t off = (int64_t)(b * kBlock + min(row, kmax)) * row_stride + 8 * lc;
+    dma16(kbase + off, t.k + piece * 512);
+    dma16(vbase + off, t.v + piece * 512);
+  }
+}
+
+
 // acc + sum of the 8 bf16 values of v (dot products with (1, 1) on bf16 pairs).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
