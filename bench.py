@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "single8k"
 KERNEL_FILES = {"forward": "forward.hip", "bwd_main": "backward.hip", "bwd_dq": "dq.hip"}
-KERNEL_NAMES = {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128>",
+KERNEL_NAMES = {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128>",
                 "bwd_dq": "dq_kernel<128>"}
 
 
@@ -203,7 +203,9 @@ def main() -> int:
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops[dominant], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops[dominant] / PEAK_BF16_TFLOPS, 4),
-                     "kernel": KERNEL_NAMES[dominant], "traffic": measured_traffic(dominant)},
+                     "kernel": ("backward_main_kernel<128, true>" if dominant == "bwd_main" and
+                                dq_mode == B.DQ_ATOMIC_POOL else KERNEL_NAMES[dominant]),
+                     "traffic": measured_traffic(dominant) if dq_mode == B.DQ_RECOMPUTE else None},
     }
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20

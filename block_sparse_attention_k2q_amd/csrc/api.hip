@@ -119,8 +119,8 @@ int msa_backward_main(const msa_problem* p, const void* q, const void* k, const 
   if (st != MSA_OK) return st;
   if (!cu_seqlens || !sched || (p->total_tokens > 0 && (!q || !k || !v || !dout || !lse || !scratch)))
     return MSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(scratch) ||
-      !aligned16(sched))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(scratch) || !aligned16(sched))
     return MSA_ERR_ALIGN;
   const msa_schedule_layout L = msa::schedule_layout(*p);
   return hip_status(msa::launch_backward_main(*p, q, k, v, dout, lse, cu_seqlens, sched, L, scratch,

@@ -400,6 +400,299 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
   if (cur_i >= 0) flush();
 }
 
+// ---------------------------------------------------------------------------
+// Main kernel of the MSA_DQ_RECOMPUTE mode: S^T, dP^T, dV, dK only.
+//
+// Two workgroups share each walk: workgroup 2x + half takes query rows
+// 64*half .. 64*half + 63 (tokens 4*half .. 4*half + 3 of the chunk, all 16
+// heads of the index head) of every task tile of walk x and accumulates its
+// own partial dK / dV of the bucket.  Each workgroup then needs under 80 KB
+// of LDS and under 256 registers per lane, so two run on every CU and the
+// softmax arithmetic of one overlaps the matrix-core work of the other.
+//
+//  * wave w handles queries 32*(w & 1) .. +31 of the half against keys
+//    32*(w >> 1) .. +31 of the block: K and V of those keys live in
+//    registers as the A operands of S^T = K Q^T and dP^T = V dO^T (loaded
+//    once per bucket segment), each lane owning one query column;
+//  * the Q and dO rows of the half (and its LSE / Delta) arrive in LDS by
+//    direct global->LDS loads into one of two swizzled buffers, the next
+//    task's copy in flight while the current one is consumed;
+//  * P^T goes to an LDS tile for dV += P^T dO, then dS^T (kept in
+//    registers meanwhile) overwrites it for dK += dS^T Q; each wave owns
+//    2 (head dim 128) or 1 (head dim 64) of the 32 x 32 output tiles of dV
+//    and of dK.
+// ---------------------------------------------------------------------------
+constexpr int kHalfM = kTileM / 2;
+
+template <int D>
+struct KvHalf {
+  bf16 q[kHalfM * D];
+  bf16 dout[kHalfM * D];
+  float lse[kHalfM];
+  float delta[kHalfM];
+};
+
+template <int D>
+struct KvSmem {
+  KvHalf<D> tile[2];
+  bf16 pd[kHalfM * kBlock];     // P^T, then dS^T, of the current half tile (rows = queries)
+  int meta[kMaxWalk][8];        // per walked task: i, r, qb, qc, d, b, tok0, len
+};
+
+// Copy the Q / dO rows, LSE and Delta of one half task tile into a swizzled
+// buffer.  Rows past the document end read the chunk's last valid row
+// (their probabilities are forced to 0 by the consumer).
+template <int D>
+__device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__ q,
+                                          const bf16* __restrict__ dout, const float* __restrict__ lse,
+                                          const float* __restrict__ delta, const int* m, int half, int Hq,
+                                          int w, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 64 / CPR;                 // rows per wave-sized piece
+  constexpr int PIECES = kHalfM / RPP;          // pieces per tensor
+  static_assert(PIECES % 4 == 0, "pieces split evenly over 4 waves");
+  const int i = m[0], qb = m[2], qc = m[3], tok0 = m[6];
+  const int lrow = lane / CPR, pcol = lane % CPR;
+#pragma unroll
+  for (int n = 0; n < PIECES / 4; ++n) {
+    const int piece = n * 4 + w;
+    const int row = piece * RPP + lrow;         // local row = (token - 4*half) * 16 + head
+    const int j = min(4 * half + (row >> 4), qc - 1);
+    const int lc = pcol ^ chunk_swizzle<CPR>(row);
+    const int64_t off = ((int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + (row & 15)) * D + 8 * lc;
+    dma16(q + off, t.q + piece * 512);
+    dma16(dout + off, t.dout + piece * 512);
+  }
+  if (w < 2 && lane < 16) {
+    // lane L copies local rows 4L..4L+3 (token L/4 of the half, heads 4(L%4)..): 16 bytes
+    const int j = min(4 * half + (lane >> 2), qc - 1);
+    const int64_t off = (int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + 4 * (lane & 3);
+    dma16((w == 0 ? lse : delta) + off, w == 0 ? (void*)t.lse : (void*)t.delta);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
+    const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dk_acc,
+    float* __restrict__ dv_acc, int Hkv, float scale) {
+  using S = KvSmem<D>;
+  constexpr int CPR = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int OUT_TILES = 2 * NT / 4;        // dV (and dK) output tiles per wave
+  static_assert(NT == 4 || NT == 2, "head dim 128 or 64");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
+  S& sm = *reinterpret_cast<S*>(smem_raw);
+
+  if (err[1]) return;
+  const int grid_walks = desc[5];
+  const int wg = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
+  if (wg >= grid_walks) return;
+  const int rpc = desc[1], full = desc[2], tail = desc[3], tail_walks = desc[4];
+  int lo, hi;
+  if (wg < full) {
+    lo = wg * rpc;
+    hi = lo + rpc;
+  } else {
+    const int t = wg - full;
+    const int base = tail / tail_walks, extra = tail % tail_walks;
+    lo = full * rpc + t * base + min(t, extra);
+    hi = lo + base + (t < extra ? 1 : 0);
+  }
+
+  const int w = wave_id(), lane = lane_id();
+  const int n32 = lane & 31, h = lane >> 5;
+  const int Hq = Hkv * kQPerKV;
+  const float c2 = scale * kLog2e;
+  const int mq = 32 * (w & 1) + n32;           // this lane's query row in the half tile
+  const int kh = w >> 1;                       // this wave's 32-key half of the block
+  const int jtok = 4 * half + (mq >> 4);       // its token within the chunk
+
+  int own_mt[OUT_TILES], own_nt[OUT_TILES];
+#pragma unroll
+  for (int x = 0; x < OUT_TILES; ++x) {
+    const int tile = w * OUT_TILES + x;
+    own_nt[x] = tile / 2;
+    own_mt[x] = tile % 2;
+  }
+  floatx16 acc_dv[OUT_TILES], acc_dk[OUT_TILES];
+  bf16x8 ka[KS], va[KS];                       // K, V rows of this wave's keys as MFMA A operands
+  int cur_i = -1, cur_r = -1, cur_tok0 = 0, cur_len = 0, cur_b = 0;
+
+  auto flush = [&]() {
+    // Partial dK/dV of the finished bucket segment; keys past the document
+    // end hold exact zeros and are sent to the block's first key.  Register
+    // j of tile x holds key 32 mt + 4h + c_j, c_j = 8(j/4) + j%4.
+    const int stride = Hkv * D;
+#pragma unroll
+    for (int x = 0; x < OUT_TILES; ++x) {
+      int kb = 32 * own_mt[x] + 4 * h;
+      asm volatile("" : "+v"(kb));   // keep the per-register offsets below out of the task loop
+      const int64_t first = ((int64_t)(cur_tok0 + cur_b * kBlock) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
+      float* dvp = dv_acc + first;
+      float* dkp = dk_acc + first;
+      const int room = cur_len - cur_b * kBlock - kb;   // c_j < room: key inside the document
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int c = 8 * (j >> 2) + (j & 3);
+        const int rel = c < room ? (kb + c) * stride : 0;
+        atomicAdd(dvp + rel, acc_dv[x][j]);
+        atomicAdd(dkp + rel, acc_dk[x][j]);
+      }
+    }
+  };
+
+  const int nrows = hi - lo;
+  for (int e = threadIdx.x; e < nrows; e += kBwdThreads) {
+    const int32_t* tm = task_meta + (int64_t)(lo + e) * 6;
+    int* m = sm.meta[e];
+#pragma unroll
+    for (int x = 0; x < 6; ++x) m[x] = tm[x];
+    const int d = tm[4];
+    const int t0 = cu[d];
+    m[6] = t0;
+    m[7] = cu[d + 1] - t0;
+  }
+  lds_barrier();
+  if (nrows > 0) stage_qdo<D>(sm.tile[0], q, dout, lse, delta, sm.meta[0], half, Hq, w, lane);
+
+  for (int row = lo; row < hi; ++row) {
+    const int e = row - lo;
+    const int* mrow = sm.meta[e];
+    // wave-uniform task fields, kept in scalar registers
+    const int i = __builtin_amdgcn_readfirstlane(mrow[0]), r = __builtin_amdgcn_readfirstlane(mrow[1]);
+    const int qb = __builtin_amdgcn_readfirstlane(mrow[2]), qc = __builtin_amdgcn_readfirstlane(mrow[3]);
+    const int b = __builtin_amdgcn_readfirstlane(mrow[5]);
+    const int tok0 = __builtin_amdgcn_readfirstlane(mrow[6]), len = __builtin_amdgcn_readfirstlane(mrow[7]);
+    KvHalf<D>& T = sm.tile[e & 1];
+    wait_vmem();
+    lds_barrier();   // task e landed; every wave is done with task e-1 and with pd
+
+    if (i != cur_i || r != cur_r) {
+      if (cur_i >= 0) flush();
+#pragma unroll
+      for (int x = 0; x < OUT_TILES; ++x) {
+        acc_dv[x] = floatx16{};
+        acc_dk[x] = floatx16{};
+      }
+      cur_i = i; cur_r = r; cur_tok0 = tok0; cur_len = len; cur_b = b;
+      // K, V row 32*kh + n32 of the block, d = 16s + 8h .. +7 (keys past the
+      // document end read its last key; they are masked).
+      const int key = min(b * kBlock + 32 * kh + n32, len - 1);
+      const int64_t off = ((int64_t)(tok0 + key) * Hkv + i) * D + 8 * h;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        ka[s] = load_bf16x8(k + off + 16 * s);
+        va[s] = load_bf16x8(v + off + 16 * s);
+      }
+    }
+    if (row + 1 < hi)
+      stage_qdo<D>(sm.tile[(e + 1) & 1], q, dout, lse, delta, sm.meta[e + 1], half, Hq, w, lane);
+    if (4 * half >= qc) continue;   // this half holds no token of the chunk
+
+    // --- S^T and dP^T: 32 keys x 32 queries per wave ---------------------------
+    floatx16 st = floatx16{}, dpt = floatx16{};
+    {
+      bf16x8 bq[2], bo[2];
+      bq[0] = lds_row8<CPR>(T.q, mq, 8 * h);
+      bo[0] = lds_row8<CPR>(T.dout, mq, 8 * h);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) {
+          bq[(s + 1) & 1] = lds_row8<CPR>(T.q, mq, 16 * (s + 1) + 8 * h);
+          bo[(s + 1) & 1] = lds_row8<CPR>(T.dout, mq, 16 * (s + 1) + 8 * h);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        st = mfma32(ka[s], bq[s & 1], st);
+        dpt = mfma32(va[s], bo[s & 1], dpt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Rows past the document end: LSE = +inf, so P = 0 (and dS = 0).
+    const float lv = T.lse[mq];
+    const float l2 = (jtok < qc && lv != -INFINITY) ? lv * kLog2e : INFINITY;
+    const float dl = T.delta[mq];
+    // Only the diagonal block holds keys after a query (or past the document
+    // end): there, keys at block offset > klim get score -inf, so P = 0.
+    if ((b + 1) * kBlock - 1 > qb) {
+      // key offset of register j: 32kh + 4h + 8(j/4) + j%4
+      const int klim = min(qb + jtok, len - 1) - b * kBlock - 32 * kh - 4 * h;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) st[j] = 8 * (j >> 2) + (j & 3) <= klim ? st[j] : -INFINITY;
+    }
+    bf16x4 ds4[4];
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      bf16x4 p4;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int j = 4 * jg + rr;
+        const float pv = fast_exp2(fmaf(st[j], c2, -l2));
+        p4[rr] = (bf16)pv;
+        ds4[jg][rr] = (bf16)(pv * (dpt[j] - dl));
+      }
+      // P row of this query, keys 32kh + 8jg + 4h .. +3
+      store_bf16x4(sm.pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), p4);
+    }
+    lds_barrier();   // P complete
+
+    // --- dV += P^T dO over the 64 query rows of the half ------------------------
+    {
+      const int nt = own_nt[0];
+      bf16x8 ap[2][OUT_TILES], bo[2];
+      auto load_u = [&](int u, int slot) {
+#pragma unroll
+        for (int x = 0; x < OUT_TILES; ++x)
+          ap[slot][x] = lds_tr_operand_swz<8>(sm.pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+                                              16 * u + 4, 16 * u + 12);
+        bo[slot] = lds_tr_operand_swz<CPR>(T.dout, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                           16 * u + 12);
+      };
+      load_u(0, 0);
+#pragma unroll
+      for (int u = 0; u < kHalfM / 16; ++u) {
+        if (u + 1 < kHalfM / 16) load_u(u + 1, (u + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < OUT_TILES; ++x) acc_dv[x] = mfma32(ap[u & 1][x], bo[u & 1], acc_dv[x]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    lds_barrier();   // every wave is done reading P
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) store_bf16x4(sm.pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), ds4[jg]);
+    lds_barrier();   // dS complete
+
+    // --- dK += dS^T Q over the 64 query rows of the half ------------------------
+    {
+      const int nt = own_nt[0];
+      bf16x8 ad[2][OUT_TILES], bq[2];
+      auto load_u = [&](int u, int slot) {
+#pragma unroll
+        for (int x = 0; x < OUT_TILES; ++x)
+          ad[slot][x] = lds_tr_operand_swz<8>(sm.pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+                                              16 * u + 4, 16 * u + 12);
+        bq[slot] = lds_tr_operand_swz<CPR>(T.q, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
+                                           16 * u + 12);
+      };
+      load_u(0, 0);
+#pragma unroll
+      for (int u = 0; u < kHalfM / 16; ++u) {
+        if (u + 1 < kHalfM / 16) load_u(u + 1, (u + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int x = 0; x < OUT_TILES; ++x) acc_dk[x] = mfma32(ad[u & 1][x], bq[u & 1], acc_dk[x]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (cur_i >= 0) flush();
+}
+
 }  // namespace
 
 hipError_t launch_backward_preprocess(const msa_problem& p, const void* out, const void* dout,
@@ -442,13 +735,24 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        (float*)(base + S.dv_acc), p.num_kv_heads, p.softmax_scale);
     return hipGetLastError();
   };
-  const bool atomic_dq = p.dq_mode == MSA_DQ_ATOMIC_POOL;
-  if (p.head_dim == 128) {
-    return atomic_dq ? go(backward_main_kernel<128, true>, sizeof(BwdSmem<128>))
-                     : go(backward_main_kernel<128, false>, sizeof(BwdSmem<128>));
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL) {
+    if (p.head_dim == 128) return go(backward_main_kernel<128, true>, sizeof(BwdSmem<128>));
+    return go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>));
   }
-  return atomic_dq ? go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>))
-                   : go(backward_main_kernel<64, false>, sizeof(BwdSmem<64>));
+  // Two workgroups per walk, one per query half of every task tile.
+  auto go_kv = [&](auto kern, size_t lds) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads), lds, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
+                       (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
+                       sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
+                       p.num_kv_heads, p.softmax_scale);
+    return hipGetLastError();
+  };
+  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128>, sizeof(KvSmem<128>));
+  return go_kv(backward_kv_kernel<64>, sizeof(KvSmem<64>));
 }
 
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
