@@ -428,24 +428,14 @@ template <int D>
 struct KvHalf {
   bf16 q[kHalfM * D];
   bf16 dout[kHalfM * D];
-  float lse[kHalfM];
-  float delta[kHalfM];
 };
 
-template <int D>
-struct KvSmem {
-  KvHalf<D> tile[2];
-  bf16 pd[kHalfM * kBlock];     // P^T, then dS^T, of the current half tile (rows = queries)
-  int meta[kMaxWalk][8];        // per walked task: i, r, qb, qc, d, b, tok0, len
-};
-
-// Copy the Q / dO rows, LSE and Delta of one half task tile into a swizzled
-// buffer.  Rows past the document end read the chunk's last valid row
-// (their probabilities are forced to 0 by the consumer).
+// Copy the Q / dO rows of one half task tile into a swizzled buffer.  Rows
+// past the document end read the chunk's last valid row (their
+// probabilities are forced to 0 by the consumer).
 template <int D>
 __device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__ q,
-                                          const bf16* __restrict__ dout, const float* __restrict__ lse,
-                                          const float* __restrict__ delta, const int* m, int half, int Hq,
+                                          const bf16* __restrict__ dout, const int* m, int half, int Hq,
                                           int w, int lane) {
   constexpr int CPR = D / 8;
   constexpr int RPP = 64 / CPR;                 // rows per wave-sized piece
@@ -463,12 +453,6 @@ __device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__
     dma16(q + off, t.q + piece * 512);
     dma16(dout + off, t.dout + piece * 512);
   }
-  if (w < 2 && lane < 16) {
-    // lane L copies local rows 4L..4L+3 (token L/4 of the half, heads 4(L%4)..): 16 bytes
-    const int j = min(4 * half + (lane >> 2), qc - 1);
-    const int64_t off = (int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + 4 * (lane & 3);
-    dma16((w == 0 ? lse : delta) + off, w == 0 ? (void*)t.lse : (void*)t.delta);
-  }
 }
 
 template <int D>
@@ -478,14 +462,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dk_acc,
     float* __restrict__ dv_acc, int Hkv, float scale) {
-  using S = KvSmem<D>;
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
   constexpr int OUT_TILES = 2 * NT / 4;        // dV (and dK) output tiles per wave
   static_assert(NT == 4 || NT == 2, "head dim 128 or 64");
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-  S& sm = *reinterpret_cast<S*>(smem_raw);
+  // Separate objects, so the compiler can tell the copy into one buffer
+  // from reads of the other (and of pd) and waits only where needed.
+  __shared__ __attribute__((aligned(16))) KvHalf<D> tile0;
+  __shared__ __attribute__((aligned(16))) KvHalf<D> tile1;
+  __shared__ __attribute__((aligned(16))) bf16 pd[kHalfM * kBlock];  // P^T, then dS^T (rows = queries)
+  __shared__ int meta[kMaxWalk][8];   // per walked task: i, r, qb, qc, d, b, tok0, len
 
   if (err[1]) return;
   const int grid_walks = desc[5];
@@ -549,7 +536,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
   const int nrows = hi - lo;
   for (int e = threadIdx.x; e < nrows; e += kBwdThreads) {
     const int32_t* tm = task_meta + (int64_t)(lo + e) * 6;
-    int* m = sm.meta[e];
+    int* m = meta[e];
 #pragma unroll
     for (int x = 0; x < 6; ++x) m[x] = tm[x];
     const int d = tm[4];
@@ -558,17 +545,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     m[7] = cu[d + 1] - t0;
   }
   lds_barrier();
-  if (nrows > 0) stage_qdo<D>(sm.tile[0], q, dout, lse, delta, sm.meta[0], half, Hq, w, lane);
+  // LSE and Delta of this lane's query row, fetched one task ahead.
+  auto row_index = [&](const int* m) {
+    return (int64_t)(m[6] + m[2] + min(jtok, m[3] - 1)) * Hq + kQPerKV * m[0] + (mq & 15);
+  };
+  float next_lse = 0.f, next_delta = 0.f;
+  if (nrows > 0) {
+    stage_qdo<D>(tile0, q, dout, meta[0], half, Hq, w, lane);
+    next_lse = lse[row_index(meta[0])];
+    next_delta = delta[row_index(meta[0])];
+  }
 
-  for (int row = lo; row < hi; ++row) {
+  // One task: T holds its half tile, N receives the next task's.
+  auto step = [&](int row, KvHalf<D>& T, KvHalf<D>& N) {
     const int e = row - lo;
-    const int* mrow = sm.meta[e];
+    const int* mrow = meta[e];
     // wave-uniform task fields, kept in scalar registers
     const int i = __builtin_amdgcn_readfirstlane(mrow[0]), r = __builtin_amdgcn_readfirstlane(mrow[1]);
     const int qb = __builtin_amdgcn_readfirstlane(mrow[2]), qc = __builtin_amdgcn_readfirstlane(mrow[3]);
     const int b = __builtin_amdgcn_readfirstlane(mrow[5]);
     const int tok0 = __builtin_amdgcn_readfirstlane(mrow[6]), len = __builtin_amdgcn_readfirstlane(mrow[7]);
-    KvHalf<D>& T = sm.tile[e & 1];
     wait_vmem();
     lds_barrier();   // task e landed; every wave is done with task e-1 and with pd
 
@@ -589,10 +585,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
         ka[s] = load_bf16x8(k + off + 16 * s);
         va[s] = load_bf16x8(v + off + 16 * s);
       }
+      // Wait here, before the next task's copy is issued: a wait placed by
+      // the compiler at the first use would also wait for that copy.
+      wait_vmem();
     }
-    if (row + 1 < hi)
-      stage_qdo<D>(sm.tile[(e + 1) & 1], q, dout, lse, delta, sm.meta[e + 1], half, Hq, w, lane);
-    if (4 * half >= qc) continue;   // this half holds no token of the chunk
+    const float lv = next_lse, dl = next_delta;
+    if (row + 1 < hi) {
+      stage_qdo<D>(N, q, dout, meta[e + 1], half, Hq, w, lane);
+      next_lse = lse[row_index(meta[e + 1])];
+      next_delta = delta[row_index(meta[e + 1])];
+    }
+    if (4 * half >= qc) return;   // this half holds no token of the chunk
 
     // --- S^T and dP^T: 32 keys x 32 queries per wave ---------------------------
     floatx16 st = floatx16{}, dpt = floatx16{};
@@ -613,9 +616,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       }
     }
     // Rows past the document end: LSE = +inf, so P = 0 (and dS = 0).
-    const float lv = T.lse[mq];
     const float l2 = (jtok < qc && lv != -INFINITY) ? lv * kLog2e : INFINITY;
-    const float dl = T.delta[mq];
     // Only the diagonal block holds keys after a query (or past the document
     // end): there, keys at block offset > klim get score -inf, so P = 0.
     if ((b + 1) * kBlock - 1 > qb) {
@@ -636,9 +637,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
         ds4[jg][rr] = (bf16)(pv * (dpt[j] - dl));
       }
       // P row of this query, keys 32kh + 8jg + 4h .. +3
-      store_bf16x4(sm.pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), p4);
+      store_bf16x4(pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), p4);
     }
-    lds_barrier();   // P complete
+    lds_sync();      // P complete
 
     // --- dV += P^T dO over the 64 query rows of the half ------------------------
     {
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       auto load_u = [&](int u, int slot) {
 #pragma unroll
         for (int x = 0; x < OUT_TILES; ++x)
-          ap[slot][x] = lds_tr_operand_swz<8>(sm.pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+          ap[slot][x] = lds_tr_operand_swz<8>(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
                                               16 * u + 4, 16 * u + 12);
         bo[slot] = lds_tr_operand_swz<CPR>(T.dout, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
                                            16 * u + 12);
@@ -662,10 +663,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    lds_barrier();   // every wave is done reading P
+    lds_sync();      // every wave is done reading P
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) store_bf16x4(sm.pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), ds4[jg]);
-    lds_barrier();   // dS complete
+    for (int jg = 0; jg < 4; ++jg) store_bf16x4(pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), ds4[jg]);
+    lds_sync();      // dS complete
 
     // --- dK += dS^T Q over the 64 query rows of the half ------------------------
     {
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       auto load_u = [&](int u, int slot) {
 #pragma unroll
         for (int x = 0; x < OUT_TILES; ++x)
-          ad[slot][x] = lds_tr_operand_swz<8>(sm.pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+          ad[slot][x] = lds_tr_operand_swz<8>(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
                                               16 * u + 4, 16 * u + 12);
         bq[slot] = lds_tr_operand_swz<CPR>(T.q, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
                                            16 * u + 12);
@@ -689,6 +690,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int row = lo; row < hi; row += 2) {
+    step(row, tile0, tile1);
+    if (row + 1 < hi) step(row + 1, tile1, tile0);
   }
   if (cur_i >= 0) flush();
 }
@@ -740,19 +745,16 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
     return go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>));
   }
   // Two workgroups per walk, one per query half of every task tile.
-  auto go_kv = [&](auto kern, size_t lds) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads), lds, stream, (const bf16*)q,
+  auto go_kv = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
                        p.num_kv_heads, p.softmax_scale);
     return hipGetLastError();
   };
-  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128>, sizeof(KvSmem<128>));
-  return go_kv(backward_kv_kernel<64>, sizeof(KvSmem<64>));
+  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128>);
+  return go_kv(backward_kv_kernel<64>);
 }
 
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,

@@ -155,6 +155,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier for LDS reads and writes made by the waves themselves.  Unlike
+// lds_barrier it does not wait for direct global->LDS copies still in flight
+// (a release fence on LDS would), so a copy into another buffer keeps going
+// across it.  The "memory" clobber keeps the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+
 // K and V rows of one key block in LDS, each an unpadded swizzled tile.
 template <int D>
 struct KVTiles {
