@@ -4,9 +4,11 @@
 One step = one pass of the whole path over one batch of synthetic input that
 is already resident in HBM: schedule build (selection cleaning, k2q CSR,
 task table), sparse forward, backward preprocess, backward main kernel
-(KV-parallel: S^T, dP^T, dV, dK), backward dQ kernel (query-parallel, recomputes
-S^T and dP^T), backward postprocess.  Workload: one 8192-token document, 4 KV heads x 16
-query heads, head dim 128, key block 64, 8-query chunks, top-k 16.
+(KV-parallel: S^T, dP^T, dV, dK, and in the default dq mode "ds" each tile's
+dS stored), backward dQ kernel (query-parallel: dQ from the stored dS, or
+recomputing S^T and dP^T in mode "recompute"), backward postprocess.
+Workload: one 8192-token document, 4 KV heads x 16 query heads, head dim
+128, key block 64, 8-query chunks, top-k 16.
 
 Prints one JSON line.  ``value`` is useful TFLOP/s of forward + backward:
 every selected (index head, chunk, block) pair counts as one 128 x 64 tile,
@@ -31,8 +33,13 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "single8k"
 KERNEL_FILES = {"forward": "forward.hip", "bwd_main": "backward.hip", "bwd_dq": "dq.hip"}
-KERNEL_NAMES = {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128>",
-                "bwd_dq": "dq_kernel<128>"}
+KERNEL_NAMES = {  # per dq mode
+    "recompute": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, false>",
+                  "bwd_dq": "dq_kernel<128>"},
+    "ds": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true>",
+           "bwd_dq": "dq_from_ds_kernel<128>"},
+    "atomic": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
+}
 
 
 def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
@@ -48,11 +55,18 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def traffic_profile_path(kernel_name: str) -> str:
+    """profiles/<kernel>_single8k_hbm_traffic.md for a kernel name such as
+    'dq_kernel<128>' (non-alphanumerics become underscores)."""
+    stem = re.sub(r"[^A-Za-z0-9]+", "_", kernel_name).strip("_")
+    return os.path.join(ROOT, "profiles", f"{stem}_{WORKLOAD}_hbm_traffic.md")
+
+
+def measured_traffic(kernel: str, mode: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
     summary, or None when absent or taken on a different kernel source."""
     try:
-        with open(os.path.join(ROOT, "profiles", f"{kernel}_single8k_hbm_traffic.md")) as f:
+        with open(traffic_profile_path(KERNEL_NAMES[mode][kernel])) as f:
             text = f.read()
     except OSError:
         return None
@@ -99,7 +113,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dq-mode", choices=("recompute", "atomic"), default="recompute")
+    ap.add_argument("--dq-mode", choices=("ds", "recompute", "atomic"), default="ds")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run a plain device-to-device copy of this many MiB "
                          "three times (the known-size reference for HBM byte counters)")
@@ -118,7 +132,7 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     num_cus = B.msa_device_check(0)
     w = make_workload(WORKLOAD)
-    dq_mode = B.DQ_ATOMIC_POOL if args.dq_mode == "atomic" else B.DQ_RECOMPUTE
+    dq_mode = {"recompute": B.DQ_RECOMPUTE, "ds": B.DQ_DS_BUFFER, "atomic": B.DQ_ATOMIC_POOL}[args.dq_mode]
     p = B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk, num_cus=num_cus,
                        softmax_scale=w.scale, block_size=w.block, dq_mode=dq_mode)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
@@ -203,9 +217,8 @@ def main() -> int:
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops[dominant], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops[dominant] / PEAK_BF16_TFLOPS, 4),
-                     "kernel": ("backward_main_kernel<128, true>" if dominant == "bwd_main" and
-                                dq_mode == B.DQ_ATOMIC_POOL else KERNEL_NAMES[dominant]),
-                     "traffic": measured_traffic(dominant) if dq_mode == B.DQ_RECOMPUTE else None},
+                     "kernel": KERNEL_NAMES[args.dq_mode][dominant],
+                     "traffic": measured_traffic(dominant, args.dq_mode)},
     }
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_HIP = range(6)
 SCHED_ERR_DROPPED, SCHED_ERR_GEOMETRY = 0, 1
-DQ_RECOMPUTE, DQ_ATOMIC_POOL = 0, 1
+DQ_RECOMPUTE, DQ_ATOMIC_POOL, DQ_DS_BUFFER = 0, 1, 2
 MAX_DOC_CHUNKS = 1 << 18
 
 EXPORTED = (
@@ -138,12 +138,12 @@ class Problem:
     q_per_kv: int = 16
     block_size: int = 64
     query_chunk: int = 8
-    dq_mode: int = DQ_RECOMPUTE
+    dq_mode: int = DQ_DS_BUFFER
 
     @staticmethod
     def make(cu_seqlens, num_kv_heads: int, head_dim: int, topk: int, num_cus: int = 256,
              softmax_scale: Optional[float] = None, block_size: int = 64,
-             dq_mode: int = DQ_RECOMPUTE) -> "Problem":
+             dq_mode: int = DQ_DS_BUFFER) -> "Problem":
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         lens = np.diff(cu)
         nch = -(-lens // 8)

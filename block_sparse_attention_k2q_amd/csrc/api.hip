@@ -40,7 +40,9 @@ int check_problem(const msa_problem* p) {
       p->max_doc_chunks > p->num_chunks || (p->num_chunks > 0 && p->max_doc_chunks < 1))
     return MSA_ERR_SHAPE;
   if (!(p->softmax_scale > 0.f)) return MSA_ERR_INVALID;
-  if (p->dq_mode != MSA_DQ_RECOMPUTE && p->dq_mode != MSA_DQ_ATOMIC_POOL) return MSA_ERR_INVALID;
+  if (p->dq_mode != MSA_DQ_RECOMPUTE && p->dq_mode != MSA_DQ_ATOMIC_POOL &&
+      p->dq_mode != MSA_DQ_DS_BUFFER)
+    return MSA_ERR_INVALID;
   return MSA_OK;
 }
 

@@ -440,28 +440,32 @@ __device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__
   constexpr int CPR = D / 8;
   constexpr int RPP = 64 / CPR;                 // rows per wave-sized piece
   constexpr int PIECES = kHalfM / RPP;          // pieces per tensor
-  static_assert(PIECES % 4 == 0, "pieces split evenly over 4 waves");
-  const int i = m[0], qb = m[2], qc = m[3], tok0 = m[6];
+  static_assert(PIECES % 4 == 0 && 16 % RPP == 0, "pieces split evenly over 4 waves, within a token");
+  const int i = __builtin_amdgcn_readfirstlane(m[0]), qb = __builtin_amdgcn_readfirstlane(m[2]);
+  const int qc = __builtin_amdgcn_readfirstlane(m[3]), tok0 = __builtin_amdgcn_readfirstlane(m[6]);
   const int lrow = lane / CPR, pcol = lane % CPR;
 #pragma unroll
   for (int n = 0; n < PIECES / 4; ++n) {
     const int piece = n * 4 + w;
     const int row = piece * RPP + lrow;         // local row = (token - 4*half) * 16 + head
-    const int j = min(4 * half + (row >> 4), qc - 1);
+    // all rows of a piece belong to one token: a wave-uniform base per piece
+    const int j = min(4 * half + ((piece * RPP) >> 4), qc - 1);
+    const int64_t first = ((int64_t)(tok0 + qb + j) * Hq + kQPerKV * i) * D;
     const int lc = pcol ^ chunk_swizzle<CPR>(row);
-    const int64_t off = ((int64_t)(tok0 + qb + j) * Hq + kQPerKV * i + (row & 15)) * D + 8 * lc;
-    dma16(q + off, t.q + piece * 512);
-    dma16(dout + off, t.dout + piece * 512);
+    const uint32_t off = (uint32_t)((row & 15) * D + 8 * lc) * 2u;
+    dma16_at(q + first, off, t.q + piece * 512);
+    dma16_at(dout + first, off, t.dout + piece * 512);
   }
 }
 
-template <int D>
+template <int D, bool WRITE_DS>
 __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dk_acc,
-    float* __restrict__ dv_acc, int Hkv, float scale) {
+    float* __restrict__ dv_acc, bf16* __restrict__ ds, const int32_t* __restrict__ doc_chunk_off,
+    const int32_t* __restrict__ sel_clean, int Hkv, int C, int K, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -543,6 +547,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     const int t0 = cu[d];
     m[6] = t0;
     m[7] = cu[d + 1] - t0;
+    if constexpr (WRITE_DS) {
+      // dS slot of the task: (index head, global chunk, position of its block
+      // in the chunk's cleaned selection); the document id is not needed later.
+      const int64_t row = (int64_t)tm[0] * C + doc_chunk_off[d] + tm[2] / kChunk;
+      const int32_t* sel = sel_clean + row * K;
+      int slot = -1;
+      for (int x = 0; x < K; ++x) slot = sel[x] == tm[5] ? x : slot;
+      m[4] = slot < 0 ? -1 : (int)(row * K + slot);
+    }
   }
   lds_barrier();
   // LSE and Delta of this lane's query row, fetched one task ahead.
@@ -638,6 +651,28 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       }
       // P row of this query, keys 32kh + 8jg + 4h .. +3
       store_bf16x4(pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), p4);
+    }
+    if constexpr (WRITE_DS) {
+      // A slot holds dS in the MFMA operand order of the dQ kernel: for each
+      // 32-row block r of the tile and 16-key step u, 64 lanes x 8 bf16, lane
+      // n + 32h' carrying row 32r + n, keys 16u + {0..3, 8..11} (h' = 0) or
+      // 16u + {4..7, 12..15} (h' = 1).  This lane's row block is
+      // 2 half + (w & 1), its steps 2kh and 2kh + 1, and h' = h.
+      const int slot = __builtin_amdgcn_readfirstlane(mrow[4]);
+      if (slot >= 0) {
+        bf16* dst = ds + (int64_t)slot * (kDsSlotBytes / 2) +
+                    ((2 * half + (w & 1)) * 4 + 2 * kh) * 512 + lane * 8;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 v8;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v8[r] = ds4[2 * t][r];
+            v8[4 + r] = ds4[2 * t + 1][r];
+          }
+          store_bf16x8(dst + 512 * t, v8);
+        }
+      }
     }
     lds_sync();      // P complete
 
@@ -750,11 +785,16 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
-                       p.num_kv_heads, p.softmax_scale);
+                       (bf16*)(base + S.ds), sched + L.doc_chunk_off, sched + L.sel_clean,
+                       p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
     return hipGetLastError();
   };
-  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128>);
-  return go_kv(backward_kv_kernel<64>);
+  if (p.dq_mode == MSA_DQ_DS_BUFFER) {
+    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true>);
+    return go_kv(backward_kv_kernel<64, true>);
+  }
+  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, false>);
+  return go_kv(backward_kv_kernel<64, false>);
 }
 
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,

@@ -61,14 +61,9 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
   const int qcount = min(kChunk, len - p0);
   const int Hq = Hkv * kQPerKV;
 
-  if (threadIdx.x == 0) {
-    int n = 0;
-    const int32_t* row = sel_clean + ((int64_t)i * C + g) * K;
-    for (int s = 0; s < K; ++s) {
-      const int b = row[s];
-      if (b >= 0) s_blocks[n++] = b;
-    }
-    s_nblocks = n;
+  if (threadIdx.x < 64) {
+    const int n = compact_selection(sel_clean + ((int64_t)i * C + g) * K, K, threadIdx.x, s_blocks, nullptr);
+    if (threadIdx.x == 0) s_nblocks = n;
   }
 
   const int w = wave_id(), lane = lane_id();
@@ -102,7 +97,8 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
 
   lds_barrier();
   const int nblk = s_nblocks;
-  if (nblk > 0) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[0], Hkv, i, w, lane);
+  const KvCopier<D, NW> copy_kv(Hkv, w, lane);
+  if (nblk > 0) copy_kv(buf0, k, v, tok0, len, s_blocks[0], i);
 
   auto consume = [&](const KVTiles<D>& t, int b) {
     // S^T = K Q^T: two 32-key tiles x two query columns; operands of k step
@@ -202,12 +198,12 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
     // Even blocks use buf0, odd blocks buf1.
     wait_vmem();
     lds_barrier();   // block bi landed in buf0; all waves are done with buf1
-    if (bi + 1 < nblk) stage_kv<D, NW>(buf1, k, v, tok0, len, s_blocks[bi + 1], Hkv, i, w, lane);
+    if (bi + 1 < nblk) copy_kv(buf1, k, v, tok0, len, s_blocks[bi + 1], i);
     consume(buf0, s_blocks[bi]);
     if (bi + 1 < nblk) {
       wait_vmem();
       lds_barrier();  // block bi+1 landed in buf1; all waves are done with buf0
-      if (bi + 2 < nblk) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[bi + 2], Hkv, i, w, lane);
+      if (bi + 2 < nblk) copy_kv(buf0, k, v, tok0, len, s_blocks[bi + 2], i);
       consume(buf1, s_blocks[bi + 1]);
     }
   }

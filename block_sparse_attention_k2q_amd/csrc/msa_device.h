@@ -170,11 +170,10 @@ struct KVTiles {
   bf16 v[kBlock * D];
 };
 
-// Copy key block b (K and V rows of KV head i) into a swizzled tile pair.
-// Keys past the document end read the document's last key instead: they are
-// masked out of the softmax, and their values are finite.
-// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
-// 64 / CPR rows); lane l supplies physical chunk l of its piece.
+// Copy key block b (K and V rows of KV head i) into a swizzled tile pair with
+// 64-bit addresses computed per copy (for kernels with no registers to hold
+// precomputed offsets).  Keys past the document end read the document's last
+// key instead: they are masked out of the softmax, and their values are finite.
 template <int D, int NWAVES>
 __device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__ k,
                                          const bf16* __restrict__ v, int tok0, int len, int b, int Hkv,
@@ -198,6 +197,98 @@ __device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__
   }
 }
 
+// Direct global -> LDS copy of 16 bytes per lane from a wave-uniform base
+// plus a per-lane 32-bit byte offset: the scalar-base addressing form of the
+// load, so no 64-bit address arithmetic runs per copy.
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t byte_off, void* lds_wave_base) {
+  dma16((const char*)sbase + byte_off, lds_wave_base);
+}
+
+// Copies of key blocks (K and V rows of KV head i) into swizzled tile pairs.
+// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
+// 64 / CPR rows); lane l supplies physical chunk l of its piece.  The lane's
+// byte offsets relative to a block's first key are computed once; keys past
+// the document end (last block of a document only) read the document's last
+// key instead: they are masked out of the softmax, and their values are finite.
+template <int D, int NWAVES>
+struct KvCopier {
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int RPP = 64 / CPR;            // rows per piece
+  static constexpr int N = kBlock / RPP / NWAVES;  // pieces per wave and tensor
+  uint32_t off[N];
+  int hkv, row_stride, w, lane;
+
+  __device__ __forceinline__ KvCopier(int Hkv, int w_, int lane_)
+      : hkv(Hkv), row_stride(Hkv * D), w(w_), lane(lane_) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) off[n] = byte_offset(n, row_of(n));
+  }
+  __device__ __forceinline__ int row_of(int n) const { return (n * NWAVES + w) * RPP + lane / CPR; }
+  __device__ __forceinline__ uint32_t byte_offset(int n, int r) const {
+    const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row_of(n));
+    return (uint32_t)(r * row_stride + 8 * lc) * 2u;
+  }
+  __device__ __forceinline__ void operator()(KVTiles<D>& t, const bf16* __restrict__ k,
+                                             const bf16* __restrict__ v, int tok0, int len, int b,
+                                             int i) const {
+    const int64_t first = ((int64_t)(tok0 + b * kBlock) * hkv + i) * D;
+    const bf16* kb = k + first;
+    const bf16* vb = v + first;
+    const int kmax = len - 1 - b * kBlock;       // last valid key offset in this block
+    if (kmax >= kBlock - 1) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const int piece = n * NWAVES + w;
+        dma16_at(kb, off[n], t.k + piece * 512);
+        dma16_at(vb, off[n], t.v + piece * 512);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const int piece = n * NWAVES + w;
+        const uint32_t o = byte_offset(n, min(row_of(n), kmax));
+        dma16_at(kb, o, t.k + piece * 512);
+        dma16_at(vb, o, t.v + piece * 512);
+      }
+    }
+  }
+};
+
+// Copy key block b of one tensor (K, say) of KV head i into a swizzled
+// kBlock x D tile; same piece layout and end-of-document rule as KvCopier.
+template <int D, int NWAVES>
+__device__ __forceinline__ void stage_block(bf16* tile, const bf16* __restrict__ src, int tok0, int len,
+                                            int b, int Hkv, int i, int w, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPP = 64 / CPR;
+  constexpr int N = kBlock / RPP / NWAVES;
+  const bf16* first = src + ((int64_t)(tok0 + b * kBlock) * Hkv + i) * D;
+  const int kmax = len - 1 - b * kBlock;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int piece = n * NWAVES + w;
+    const int row = piece * RPP + lane / CPR;
+    const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row);
+    const uint32_t o = (uint32_t)(min(row, kmax) * Hkv * D + 8 * lc) * 2u;
+    dma16_at(first, o, tile + piece * 512);
+  }
+}
+
+// Kept block ids of one cleaned selection row (K <= 64 slots, -1 = empty),
+// compacted in slot order into blocks[] (and their slot numbers into
+// slots[] when given).  Run by all 64 lanes of one wave; returns the count.
+__device__ __forceinline__ int compact_selection(const int32_t* __restrict__ row, int K, int lane,
+                                                 int* blocks, int* slots) {
+  const int b = lane < K ? row[lane] : -1;
+  const bool keep = b >= 0;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
+  const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+  if (keep) {
+    blocks[pos] = b;
+    if (slots) slots[pos] = lane;
+  }
+  return __popcll(mask);
+}
 
 // acc + sum of the 8 bf16 values of v (dot products with (1, 1) on bf16 pairs).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {

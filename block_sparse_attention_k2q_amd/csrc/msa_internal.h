@@ -13,6 +13,9 @@ constexpr int kRowsPerWalkSmall = 4;
 constexpr int kRowsPerWalkLarge = 64;
 constexpr int kRowsPerWalkSwitch = 2400;
 
+// One dS slot of the MSA_DQ_DS_BUFFER mode: 128 tile rows x 64 keys, bf16.
+constexpr int kDsSlotBytes = 128 * 64 * 2;
+
 inline int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 // Offsets (int32 elements) of the schedule workspace tables; see msa.h.
@@ -47,7 +50,7 @@ inline int64_t grid_launch_bound(int64_t cap, int num_cus) {
 // accumulators (adjacent, so one range clears both), and the dQ pool in
 // MSA_DQ_ATOMIC_POOL mode (dq_pool == total otherwise).
 struct BackwardScratch {
-  size_t delta, dk_acc, dv_acc, dq_pool, total;
+  size_t delta, dk_acc, dv_acc, dq_pool, ds, total;
 };
 inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
@@ -60,6 +63,9 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   s.dv_acc = o; o = a256(o + 4 * T * hkv * D);
   s.dq_pool = o;
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) o = a256(o + 4 * T * hq * D);
+  s.ds = o;
+  if (p.dq_mode == MSA_DQ_DS_BUFFER)
+    o = a256(o + (size_t)kDsSlotBytes * hkv * (size_t)p.num_chunks * (size_t)p.topk);
   s.total = o;
   return s;
 }

@@ -65,7 +65,7 @@ typedef struct msa_problem {
   int32_t max_doc_chunks;  /* max_d ceil(len_d / 8); <= MSA_MAX_DOC_CHUNKS */
   int32_t num_cus;         /* compute units the walk is sized for (msa_device_check) */
   float softmax_scale;     /* usually head_dim ** -0.5 (msa_schedule: SOFTMAX_SCALE) */
-  int32_t dq_mode;         /* MSA_DQ_RECOMPUTE (default) or MSA_DQ_ATOMIC_POOL */
+  int32_t dq_mode;         /* MSA_DQ_RECOMPUTE, MSA_DQ_ATOMIC_POOL or MSA_DQ_DS_BUFFER */
 } msa_problem;
 
 /* How the backward forms dQ.
@@ -77,9 +77,15 @@ typedef struct msa_problem {
  *   lane-atomics per call on an 8K-token, 4x16-head, top-16 problem).
  * MSA_DQ_RECOMPUTE: the main kernel computes dK/dV only; msa_backward_dq runs
  *   a query-parallel kernel that recomputes S^T and dP^T per (chunk, block),
- *   accumulates dQ in registers and writes bf16 dq once (no atomics). */
+ *   accumulates dQ in registers and writes bf16 dq once (no atomics).
+ * MSA_DQ_DS_BUFFER: the main kernel also stores each tile's bf16 dS (the
+ *   same values the recompute mode forms) in a scratch buffer with one
+ *   128 x 64 slot per (index head, chunk, selection slot); msa_backward_dq
+ *   then sums dQ = scale * sum_b dS_b K_b per chunk in registers (one
+ *   contraction per tile instead of three) and writes bf16 dq once. */
 #define MSA_DQ_RECOMPUTE 0
 #define MSA_DQ_ATOMIC_POOL 1
+#define MSA_DQ_DS_BUFFER 2
 
 #define MSA_MAX_DOC_CHUNKS (1 << 18) /* documents up to 2 Mi tokens (32 KiB LDS bitmap per bucket sort) */
 
@@ -136,9 +142,10 @@ int msa_forward(const msa_problem* p, const void* q, const void* k, const void* 
                 const int32_t* cu_seqlens, const int32_t* sched, void* out, float* lse,
                 void* stream);
 
-/* Bytes of fp32 scratch msa_backward needs: Delta [T, Hq], dK and dV
- * accumulators [T, Hkv, D], and in MSA_DQ_ATOMIC_POOL mode the dQ pool
- * [T, Hq, D]. */
+/* Bytes of scratch msa_backward needs: fp32 Delta [T, Hq], fp32 dK and dV
+ * accumulators [T, Hkv, D]; in MSA_DQ_ATOMIC_POOL mode the fp32 dQ pool
+ * [T, Hq, D]; in MSA_DQ_DS_BUFFER mode the bf16 dS slots
+ * [Hkv, C, topk, 128, 64] (16 KiB per slot). */
 int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
 
 /* KV-parallel backward (msa_backward_sm100: run_backward): preprocess
@@ -146,7 +153,9 @@ int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
  * of task rows: K/V resident per bucket, bf16 MFMA contractions S^T, dP^T,
  * dV, dK per 128-row tile, dK/dV flushed per bucket segment with fp32
  * atomics; in MSA_DQ_ATOMIC_POOL mode also dQ^T per tile scattered into the
- * pool), the dQ kernel (MSA_DQ_RECOMPUTE mode), postprocess (cast to bf16).
+ * pool; in MSA_DQ_DS_BUFFER mode also each tile's bf16 dS into its slot),
+ * the dQ kernel (MSA_DQ_RECOMPUTE and MSA_DQ_DS_BUFFER modes), postprocess
+ * (cast to bf16).
  * dk/dv rows that no query attends are exactly 0. */
 int msa_backward(const msa_problem* p, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
