@@ -35,7 +35,7 @@ def test_grid_launch_bound_matches_walk_rule():
 
 
 def test_schedule_layout_is_host_only_and_sized():
-    p = B.Problem.make([0, 8192], 4, 128, 16)
+    p = B.Problem.make([0, 8192], 4, 128, 16, dq_mode=B.DQ_RECOMPUTE)
     L = B.msa_schedule_layout_of(p)
     cap = 4 * 1024 * 16
     assert L.task_meta + 6 * cap <= L.total
