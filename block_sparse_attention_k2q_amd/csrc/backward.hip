@@ -613,18 +613,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     // --- S^T and dP^T: 32 keys x 32 queries per wave ---------------------------
     floatx16 st = floatx16{}, dpt = floatx16{};
     {
-      bf16x8 bq[2], bo[2];
-      bq[0] = lds_row8<CPR>(T.q, mq, 8 * h);
-      bo[0] = lds_row8<CPR>(T.dout, mq, 8 * h);
+      // Q / dO operands two k steps ahead: one step (two MFMAs) does not
+      // cover the LDS latency.
+      bf16x8 bq[3], bo[3];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        bq[s] = lds_row8<CPR>(T.q, mq, 16 * s + 8 * h);
+        bo[s] = lds_row8<CPR>(T.dout, mq, 16 * s + 8 * h);
+      }
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) {
-          bq[(s + 1) & 1] = lds_row8<CPR>(T.q, mq, 16 * (s + 1) + 8 * h);
-          bo[(s + 1) & 1] = lds_row8<CPR>(T.dout, mq, 16 * (s + 1) + 8 * h);
+        if (s + 2 < KS) {
+          bq[(s + 2) % 3] = lds_row8<CPR>(T.q, mq, 16 * (s + 2) + 8 * h);
+          bo[(s + 2) % 3] = lds_row8<CPR>(T.dout, mq, 16 * (s + 2) + 8 * h);
         }
         __builtin_amdgcn_sched_barrier(0);
-        st = mfma32(ka[s], bq[s & 1], st);
-        dpt = mfma32(va[s], bo[s & 1], dpt);
+        st = mfma32(ka[s], bq[s % 3], st);
+        dpt = mfma32(va[s], bo[s % 3], dpt);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

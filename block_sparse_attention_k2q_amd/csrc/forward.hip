@@ -28,14 +28,18 @@ namespace msa {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;
-// One 32-query column per wave (4 waves per tile) fits 256 registers, so two
-// waves share each SIMD; two columns per wave halve the LDS reads but need
-// ~300 registers (one wave per SIMD) and measured slower.
-constexpr int kFwdNQ = 1;
+constexpr int kFwdThreads = 256;      // 4 waves, one 32-query MFMA column each
 
-// NQ = 32-query MFMA columns per wave; the 128-row tile takes 4 / NQ waves.
-template <int D, int NQ>
-__global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
+// The next kept block of a selection row: `rem` holds the not yet taken
+// slots (a wave-uniform mask), `bsel` lane s the block id of slot s.
+__device__ __forceinline__ int take_block(uint64_t& rem, int bsel) {
+  const int slot = (int)__builtin_ctzll(rem);
+  rem &= rem - 1;
+  return __builtin_amdgcn_readlane(bsel, slot);
+}
+
+template <int D>
+__global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
@@ -44,11 +48,18 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
   constexpr int NT = D / 32;           // 32-wide d tiles of O^T
-  constexpr int NW = 4 / NQ;            // waves per workgroup
-  __shared__ __attribute__((aligned(16))) KVTiles<D> buf0;
-  __shared__ __attribute__((aligned(16))) KVTiles<D> buf1;
-  __shared__ int s_blocks[64];
-  __shared__ int s_nblocks;
+  constexpr int NW = kFwdThreads / 64;
+  constexpr int kCopyOps = kBlock / (64 / CPR) / NW;   // copies per wave for one K or V tile
+  static_assert(kCopyOps < 16, "fits the low vmcnt field");
+  // K ring of three, V ring of two (80 KiB at D = 128, so two workgroups
+  // share a CU): K of block j+2 and V of block j+1 are copied while block j
+  // is consumed.  Separate objects let the compiler see that a copy into one
+  // buffer does not touch the others.
+  __shared__ __attribute__((aligned(16))) bf16 kb0[kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 kb1[kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 kb2[kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 vb0[kBlock * D];
+  __shared__ __attribute__((aligned(16))) bf16 vb1[kBlock * D];
 
   if (err[1]) return;
   const int i = blockIdx.x % Hkv;
@@ -61,171 +72,159 @@ __global__ __launch_bounds__(256 / NQ, NQ == 1 ? 2 : 1) void forward_kernel(
   const int qcount = min(kChunk, len - p0);
   const int Hq = Hkv * kQPerKV;
 
-  if (threadIdx.x < 64) {
-    const int n = compact_selection(sel_clean + ((int64_t)i * C + g) * K, K, threadIdx.x, s_blocks, nullptr);
-    if (threadIdx.x == 0) s_nblocks = n;
-  }
-
   const int w = wave_id(), lane = lane_id();
   const int n32 = lane & 31, h = lane >> 5;
-  // Query column nq of this lane: tile row 32(NQ w + nq) + n32, i.e. token
-  // 2(NQ w + nq) + n32/16 and head n32%16.
-  int jq[NQ], pq[NQ];
-  bool qvalid[NQ];
-  int64_t qrow[NQ];
-  bf16x8 qf[NQ][KS];
-#pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    jq[nq] = 2 * (NQ * w + nq) + (n32 >> 4);
-    qvalid[nq] = jq[nq] < qcount;
-    pq[nq] = p0 + jq[nq];
-    qrow[nq] = (int64_t)(tok0 + p0 + min(jq[nq], qcount - 1)) * Hq + kQPerKV * i + (n32 & 15);
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[nq][s] = qvalid[nq] ? load_bf16x8(q + qrow[nq] * D + 16 * s + 8 * h) : bf16x8{};
-  }
 
-  floatx16 o[NT][NQ];
+  // Every wave reads the selection row itself: lane s holds slot s, the
+  // kept slots form a wave-uniform mask walked in slot order.
+  const int bsel = lane < K ? sel_clean[((int64_t)i * C + g) * K + lane] : -1;
+  const uint64_t kept = __builtin_amdgcn_ballot_w64(bsel >= 0);
+  const int nblk = __popcll(kept);
+  uint64_t rem_k = kept, rem_v = kept, rem_c = kept;
+
+  // Query column of this lane: tile row 32w + n32, i.e. token 2w + n32/16
+  // and head n32%16.
+  const int jq = 2 * w + (n32 >> 4);
+  const bool qvalid = jq < qcount;
+  const int pq = p0 + jq;
+  const int64_t qrow = (int64_t)(tok0 + p0 + min(jq, qcount - 1)) * Hq + kQPerKV * i + (n32 & 15);
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int s = 0; s < KS; ++s) qf[s] = qvalid ? load_bf16x8(q + qrow * D + 16 * s + 8 * h) : bf16x8{};
+
+  floatx16 o[NT];
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) o[t][nq] = floatx16{};
-  float m[NQ], l[NQ];
-#pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) { m[nq] = -INFINITY; l[nq] = 0.f; }
+  for (int t = 0; t < NT; ++t) o[t] = floatx16{};
+  float m = -INFINITY, l = 0.f;
   const float c2 = scale * kLog2e;
 
-  lds_barrier();
-  const int nblk = s_nblocks;
-  const KvCopier<D, NW> copy_kv(Hkv, w, lane);
-  if (nblk > 0) copy_kv(buf0, k, v, tok0, len, s_blocks[0], i);
+  auto copy = [&](bf16* tile, const bf16* src, int b) {
+    stage_block<D, NW>(tile, src, tok0, len, b, Hkv, i, w, lane);
+  };
+  // Issue order K0, V0, K1, then per step V_{j+1}, K_{j+2}: when block j is
+  // due, only K_{j+1}'s copies may still be outstanding.
+  if (nblk > 0) {
+    copy(kb0, k, take_block(rem_k, bsel));
+    copy(vb0, v, take_block(rem_v, bsel));
+  }
+  if (nblk > 1) copy(kb1, k, take_block(rem_k, bsel));
 
-  auto consume = [&](const KVTiles<D>& t, int b) {
-    // S^T = K Q^T: two 32-key tiles x two query columns; operands of k step
-    // s+1 are read while step s runs.
-    floatx16 st[2][NQ];
+  auto consume = [&](const bf16* kt, const bf16* vt, int b) {
+    // S^T = K Q^T: two 32-key tiles; operands of k step s+1 are read while
+    // step s runs.
+    floatx16 st[2] = {floatx16{}, floatx16{}};
+    // K operands two k steps ahead: one step (two MFMAs) does not cover the
+    // LDS latency.
+    bf16x8 ak[3][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) st[a][nq] = floatx16{};
-    bf16x8 ak[2][2];
-    ak[0][0] = lds_row8<CPR>(t.k, n32, 8 * h);
-    ak[0][1] = lds_row8<CPR>(t.k, 32 + n32, 8 * h);
+    for (int s = 0; s < 2; ++s) {
+      ak[s][0] = lds_row8<CPR>(kt, n32, 16 * s + 8 * h);
+      ak[s][1] = lds_row8<CPR>(kt, 32 + n32, 16 * s + 8 * h);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) {
-        ak[(s + 1) & 1][0] = lds_row8<CPR>(t.k, n32, 16 * (s + 1) + 8 * h);
-        ak[(s + 1) & 1][1] = lds_row8<CPR>(t.k, 32 + n32, 16 * (s + 1) + 8 * h);
+      if (s + 2 < KS) {
+        ak[(s + 2) % 3][0] = lds_row8<CPR>(kt, n32, 16 * (s + 2) + 8 * h);
+        ak[(s + 2) % 3][1] = lds_row8<CPR>(kt, 32 + n32, 16 * (s + 2) + 8 * h);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) st[a][nq] = mfma32(ak[s & 1][a], qf[nq][s], st[a][nq]);
+      for (int a = 0; a < 2; ++a) st[a] = mfma32(ak[s % 3][a], qf[s], st[a]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Online softmax per query column.  Only the diagonal block holds keys
-    // after a query (or past the document end): there, keys at block offset
-    // > klim are set to -inf before the max.
-    const bool diag = (b + 1) * kBlock - 1 > p0;
-    bf16x8 pb[NQ][4];
-#pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) {
-      if (diag) {
-        const int klim = min(pq[nq], len - 1) - b * kBlock;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = 32 * a + 8 * (j >> 2) + 4 * h + (j & 3);
-            st[a][nq][j] = key <= klim ? st[a][nq][j] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[a][nq][j]);
-      mx = fmaxf(mx, swap_halves(mx)) * c2;   // max in the scaled log2 domain
-      // Lazy rescale: the running max m only moves when a score exceeds it by
-      // more than kRescaleLog2, so P = exp2(s - m) stays <= 2^kRescaleLog2 and
-      // the O accumulators are rescaled only on the (rare) blocks that move it.
-      const bool move = mx > m[nq] + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float m_new = move ? mx : m[nq];
-        const float alpha = (m[nq] == -INFINITY) ? 0.f : fast_exp2(m[nq] - m_new);
-        l[nq] *= alpha;
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) o[tt][nq] *= alpha;
-        m[nq] = m_new;
-      }
-      const float msub = (m[nq] == -INFINITY) ? 0.f : m[nq];
+    // Online softmax.  Only the diagonal block holds keys after a query (or
+    // past the document end): there, keys at block offset > klim are set to
+    // -inf before the max.
+    if ((b + 1) * kBlock - 1 > p0) {
+      // key offset of register j of tile a: 32a + 4h + 8(j/4) + j%4
+      const int klim = min(pq, len - 1) - b * kBlock - 4 * h;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          pb[nq][2 * a + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(st[a][nq][j], c2, -msub));
-      // Row sum of the bf16 probabilities that enter O (same values normalise it).
-#pragma unroll
-      for (int u = 0; u < 4; ++u) l[nq] = sum_bf16x8(pb[nq][u], l[nq]);
+          st[a][j] = 32 * a + 8 * (j >> 2) + (j & 3) <= klim ? st[a][j] : -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[a][j]);
+    mx = fmaxf(mx, swap_halves(mx)) * c2;   // max in the scaled log2 domain
+    // Lazy rescale: the running max m only moves when a score exceeds it by
+    // more than kRescaleLog2, so P = exp2(s - m) stays <= 2^kRescaleLog2 and
+    // the O accumulators are rescaled only on the (rare) blocks that move it.
+    const bool move = mx > m + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float m_new = move ? mx : m;
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) o[tt] *= alpha;
+      m = m_new;
+    }
+    const float msub = (m == -INFINITY) ? 0.f : m;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pb[2 * a + (j >> 3)][j & 7] = (bf16)fast_exp2(fmaf(st[a][j], c2, -msub));
+    // Row sum of the bf16 probabilities that enter O (same values normalise it).
+#pragma unroll
+    for (int u = 0; u < 4; ++u) l = sum_bf16x8(pb[u], l);
 
     // O^T += V^T P^T over 4 k steps of 16 keys; V^T operands double-buffered.
     bf16x8 av[2][NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-      av[0][tt] = lds_tr_operand_swz<CPR>(t.v, 32 * tt, lane, 0, 4, 8, 12);
+    for (int tt = 0; tt < NT; ++tt) av[0][tt] = lds_tr_operand_swz<CPR>(vt, 32 * tt, lane, 0, 4, 8, 12);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (u + 1 < 4) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
-          av[(u + 1) & 1][tt] = lds_tr_operand_swz<CPR>(t.v, 32 * tt, lane, 16 * (u + 1),
-                                                        16 * (u + 1) + 4, 16 * (u + 1) + 8,
-                                                        16 * (u + 1) + 12);
+          av[(u + 1) & 1][tt] = lds_tr_operand_swz<CPR>(vt, 32 * tt, lane, 16 * (u + 1), 16 * (u + 1) + 4,
+                                                        16 * (u + 1) + 8, 16 * (u + 1) + 12);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) o[tt][nq] = mfma32(av[u & 1][tt], pb[nq][u], o[tt][nq]);
+      for (int tt = 0; tt < NT; ++tt) o[tt] = mfma32(av[u & 1][tt], pb[u], o[tt]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  for (int bi = 0; bi < nblk; bi += 2) {
-    // Even blocks use buf0, odd blocks buf1.
-    wait_vmem();
-    lds_barrier();   // block bi landed in buf0; all waves are done with buf1
-    if (bi + 1 < nblk) copy_kv(buf1, k, v, tok0, len, s_blocks[bi + 1], i);
-    consume(buf0, s_blocks[bi]);
-    if (bi + 1 < nblk) {
-      wait_vmem();
-      lds_barrier();  // block bi+1 landed in buf1; all waves are done with buf0
-      if (bi + 2 < nblk) copy_kv(buf0, k, v, tok0, len, s_blocks[bi + 2], i);
-      consume(buf1, s_blocks[bi + 1]);
-    }
+  // Block j: K in kb<j % 3>, V in vb<j % 2>.
+  auto step = [&](int j, const bf16* kt, const bf16* vt, bf16* v_next, bf16* k_next2) {
+    if (j + 1 < nblk) __builtin_amdgcn_s_waitcnt(0x0F70 | kCopyOps);   // K_{j+1} may stay in flight
+    else wait_vmem();
+    lds_sync();   // block j landed for every wave; all are done with block j-1's buffers
+    if (j + 1 < nblk) copy(v_next, v, take_block(rem_v, bsel));
+    if (j + 2 < nblk) copy(k_next2, k, take_block(rem_k, bsel));
+    consume(kt, vt, take_block(rem_c, bsel));
+  };
+  for (int j = 0; j < nblk; j += 6) {
+    step(j, kb0, vb0, vb1, kb2);
+    if (j + 1 < nblk) step(j + 1, kb1, vb1, vb0, kb0);
+    if (j + 2 < nblk) step(j + 2, kb2, vb0, vb1, kb1);
+    if (j + 3 < nblk) step(j + 3, kb0, vb1, vb0, kb2);
+    if (j + 4 < nblk) step(j + 4, kb1, vb0, vb1, kb0);
+    if (j + 5 < nblk) step(j + 5, kb2, vb1, vb0, kb1);
   }
 
+  const float l_tot = l + swap_halves(l);
+  if (!qvalid) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  bf16* orow = out + qrow * D;
 #pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    const float l_tot = l[nq] + swap_halves(l[nq]);
-    if (!qvalid[nq]) continue;
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16* orow = out + qrow[nq] * D;
+  for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
+    for (int jg = 0; jg < 4; ++jg) {
+      bf16x4 v4;
 #pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        bf16x4 v4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = (bf16)(o[tt][nq][4 * jg + r] * inv);
-        store_bf16x4(orow + 32 * tt + 8 * jg + 4 * h, v4);
-      }
+      for (int r = 0; r < 4; ++r) v4[r] = (bf16)(o[tt][4 * jg + r] * inv);
+      store_bf16x4(orow + 32 * tt + 8 * jg + 4 * h, v4);
     }
-    if (h == 0) lse[qrow[nq]] = l_tot > 0.f ? (m[nq] + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
+  if (h == 0) lse[qrow] = l_tot > 0.f ? (m + fast_log2(l_tot)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -241,8 +240,8 @@ hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, co
                        sched + L.sel_clean, sched + L.err, (bf16*)out, lse, p.num_kv_heads,
                        p.num_chunks, p.topk, p.softmax_scale);
   };
-  if (p.head_dim == 128) args(forward_kernel<128, kFwdNQ>, 256 / kFwdNQ);
-  else args(forward_kernel<64, kFwdNQ>, 256 / kFwdNQ);
+  if (p.head_dim == 128) args(forward_kernel<128>, kFwdThreads);
+  else args(forward_kernel<64>, kFwdThreads);
   return hipGetLastError();
 }
 
