@@ -675,7 +675,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
             v8[r] = ds4[2 * t][r];
             v8[4 + r] = ds4[2 * t + 1][r];
           }
-          store_bf16x8(dst + 512 * t, v8);
+          store_bf16x8_stream(dst + 512 * t, v8);
         }
       }
     }

@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
     stage_block<D, NW>(kb, k, tok0, len, s_block[n], Hkv, i, w, lane);
     const bf16* src = ds_lane + (int64_t)s_slot[n] * (kDsSlotBytes / 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dst[u] = load_bf16x8(src + 512 * u);
+    for (int u = 0; u < 4; ++u) dst[u] = load_bf16x8_stream(src + 512 * u);
   };
   auto step = [&](int n, const bf16* kb, const bf16x8 (&dc)[4], bf16* next_kb, bf16x8 (&next_d)[4]) {
     // Block n's copies are done once at most the next block's are pending.

@@ -138,6 +138,14 @@ __device__ __forceinline__ bf16x8 load_bf16x8_lds(const bf16* p) {
 __device__ __forceinline__ void store_bf16x8(bf16* p, bf16x8 v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
+// Streaming variants (non-temporal hint): data written or read once, kept
+// from displacing data that is reused.
+__device__ __forceinline__ void store_bf16x8_stream(bf16* p, bf16x8 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ bf16x8 load_bf16x8_stream(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
 __device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
 }
