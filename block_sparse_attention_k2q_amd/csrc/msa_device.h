@@ -129,6 +129,13 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
 // Wait until this wave has no outstanding vector-memory operations.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// The compiler counts a direct global->LDS copy as an LDS-counter event as
+// well; while one is pending it waits for every outstanding LDS read
+// (lgkmcnt(0)) instead of only the one it needs.  Called right after the
+// copies are issued, at a point with no LDS reads outstanding, this wait
+// costs nothing and lets the following LDS reads be waited for one by one.
+__device__ __forceinline__ void after_lds_copies() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
@@ -145,6 +152,9 @@ __device__ __forceinline__ void store_bf16x8_stream(bf16* p, bf16x8 v) {
 }
 __device__ __forceinline__ bf16x8 load_bf16x8_stream(const bf16* p) {
   return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void store_bf16x4_stream(bf16* p, bf16x4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
 }
 __device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
@@ -297,6 +307,60 @@ __device__ __forceinline__ int compact_selection(const int32_t* __restrict__ row
   }
   return __popcll(mask);
 }
+
+// Register-staged copy of key block b (K and V rows of KV head i) into
+// swizzled kBlock x D tiles (same piece layout and end-of-document rule as
+// stage_block): load_k() / load_v() issue plain 16-byte global loads into
+// registers, store_k() / store_v() write them to LDS once they have arrived.  Unlike
+// direct global->LDS copies, the loads leave the LDS alone until the wave
+// writes.  Addresses are a wave-uniform base plus this lane's 32-bit byte
+// offsets, computed once (K and V share them).
+template <int D, int NWAVES>
+struct KvStager {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPP = 64 / CPR;
+  static constexpr int N = kBlock / RPP / NWAVES;
+  bf16x8 rk[N], rv[N];
+  uint32_t off[N];
+  int hkv, w, lane;
+
+  __device__ __forceinline__ KvStager(int Hkv, int w_, int lane_) : hkv(Hkv), w(w_), lane(lane_) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) off[n] = byte_offset(n, row_of(n));
+  }
+  __device__ __forceinline__ int row_of(int n) const { return (n * NWAVES + w) * RPP + lane / CPR; }
+  __device__ __forceinline__ uint32_t byte_offset(int n, int r) const {
+    const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row_of(n));
+    return (uint32_t)(r * hkv * D + 8 * lc) * 2u;
+  }
+  // Load one tensor's rows of block b into dst (K or V: same layout).
+  __device__ __forceinline__ void load(bf16x8 (&dst)[N], const bf16* __restrict__ src, int tok0, int len,
+                                       int b, int i) const {
+    const char* base = (const char*)(src + ((int64_t)(tok0 + b * kBlock) * hkv + i) * D);
+    const int kmax = len - 1 - b * kBlock;
+    if (kmax >= kBlock - 1) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) dst[n] = load_bf16x8((const bf16*)(base + off[n]));
+    } else {
+#pragma unroll
+      for (int n = 0; n < N; ++n) dst[n] = load_bf16x8((const bf16*)(base + byte_offset(n, min(row_of(n), kmax))));
+    }
+  }
+  __device__ __forceinline__ void load_k(const bf16* __restrict__ k, int tok0, int len, int b, int i) {
+    load(rk, k, tok0, len, b, i);
+  }
+  __device__ __forceinline__ void load_v(const bf16* __restrict__ v, int tok0, int len, int b, int i) {
+    load(rv, v, tok0, len, b, i);
+  }
+  __device__ __forceinline__ void store_k(bf16* tile) const {
+#pragma unroll
+    for (int n = 0; n < N; ++n) *reinterpret_cast<bf16x8*>(tile + (n * NWAVES + w) * 512 + lane * 8) = rk[n];
+  }
+  __device__ __forceinline__ void store_v(bf16* tile) const {
+#pragma unroll
+    for (int n = 0; n < N; ++n) *reinterpret_cast<bf16x8*>(tile + (n * NWAVES + w) * 512 + lane * 8) = rv[n];
+  }
+};
 
 // acc + sum of the 8 bf16 values of v (dot products with (1, 1) on bf16 pairs).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {

@@ -13,6 +13,12 @@ constexpr int kRowsPerWalkSmall = 4;
 constexpr int kRowsPerWalkLarge = 64;
 constexpr int kRowsPerWalkSwitch = 2400;
 
+// The schedule build counts and places CSR entries with integer atomics;
+// popular rows (early key blocks) take hundreds of them, which serialise
+// per address, so every row has this many counter copies (chosen by the
+// workgroup id) and the scan adds them up.
+constexpr int kCounterCopies = 8;
+
 // One dS slot of the MSA_DQ_DS_BUFFER mode: 128 tile rows x 64 keys, bf16.
 constexpr int kDsSlotBytes = 128 * 64 * 2;
 
@@ -31,7 +37,7 @@ inline msa_schedule_layout schedule_layout(const msa_problem& p) {
   L.doc_blk_off = o; o = align64(o + p.num_docs + 1);
   L.chunk_doc = o; o = align64(o + C);
   L.sel_clean = o; o = align64(o + cap);
-  L.row_cursor = o; o = align64(o + hkv * R);
+  L.row_cursor = o; o = align64(o + kCounterCopies * hkv * R);
   L.row_ptr = o; o = align64(o + hkv * (R + 1));
   L.head_off = o; o = align64(o + hkv + 1);
   L.q_idx = o; o = align64(o + cap);

@@ -8,17 +8,21 @@
 // page (msa_task_build mirrors the walk rule on the device).
 //
 // Pipeline, all on one stream, no host synchronisation:
-//   geometry   one workgroup: per-document chunk/block offsets, checks them
-//              against the host sizes, clears the error words and counters.
+//   geometry   workgroup 0: per-document chunk/block offsets, checks them
+//              against the host sizes, clears the error words; the other
+//              workgroups clear the row counters.
 //   clean      one thread per (head, chunk, slot): keeps an id when it names
 //              a block of the document that starts at or before the chunk's
 //              last query and no earlier slot holds it; counts kept ids per
-//              key-block row with integer atomics (order-free, exact).
-//   scan       one workgroup: exclusive scan of the row counts -> row_ptr,
-//              per-head task offsets, and the walk descriptor.
-//   fill       one thread per (head, chunk, slot): places each kept entry in
-//              its row through an atomic cursor (order inside a row is not
-//              yet fixed) and writes the -1 padding.
+//              key-block row with integer atomics (order-free, exact) into
+//              one of kCounterCopies copies picked by the workgroup id.
+//   scan       one workgroup: sums the copies, exclusive scan of the row
+//              counts -> row_ptr, per-head task offsets, the walk
+//              descriptor, and each copy's fill cursor inside its row.
+//   fill       one thread per (head, chunk, slot), same workgroups as clean:
+//              places each kept entry in its row through its copy's atomic
+//              cursor (order inside a row is not yet fixed) and writes the -1
+//              padding.
 //   sort       one workgroup per (head, row): a bitmap over the document's
 //              chunks orders the row's entries ascending (entries of a row
 //              are distinct chunks), then writes the ordered q_idx and one
@@ -51,14 +55,21 @@ __device__ int block_inclusive_scan(int x, int* s_warp, int* total) {
   return x + add;
 }
 
+constexpr int kZeroPerBlock = 16 * kThreads;   // counters cleared per extra workgroup
+
 __global__ __launch_bounds__(kThreads) void geometry_kernel(
     const int32_t* __restrict__ cu, int num_docs, int T, int C, int R, int max_doc_chunks,
     int32_t* __restrict__ doc_chunk_off, int32_t* __restrict__ doc_blk_off, int32_t* __restrict__ desc,
     int32_t* __restrict__ err, int32_t* __restrict__ row_cursor, int64_t n_cursor) {
   __shared__ int s_warp[kThreads / 64];
   const int tid = threadIdx.x;
+  if (blockIdx.x > 0) {
+    const int64_t x0 = (int64_t)(blockIdx.x - 1) * kZeroPerBlock;
+    for (int x = tid; x < kZeroPerBlock; x += kThreads)
+      if (x0 + x < n_cursor) row_cursor[x0 + x] = 0;
+    return;
+  }
   if (tid < 8) { desc[tid] = 0; err[tid] = 0; }
-  for (int64_t x = tid; x < n_cursor; x += kThreads) row_cursor[x] = 0;
   int bad = 0;
   int carry_c = 0, carry_b = 0;
   for (int base = 0; base < num_docs; base += kThreads) {
@@ -99,28 +110,34 @@ __global__ __launch_bounds__(kThreads) void clean_kernel(
     int32_t* __restrict__ err) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t total = (int64_t)Hkv * C * K;
-  if (idx >= total) return;
-  const int s = (int)(idx % K);
-  const int g = (int)((idx / K) % C);
-  const int i = (int)(idx / ((int64_t)K * C));
-  const bool geom_ok = err[1] == 0;
-  int d = upper_bound_minus1(doc_chunk_off, num_docs + 1, g);
-  d = d < num_docs ? d : num_docs - 1;
-  const int c = g - doc_chunk_off[d];
-  const int len = cu[d + 1] - cu[d];
-  const int nb = (len + kBlock - 1) / kBlock;
-  const int last_q = min(kChunk * c + kChunk - 1, len - 1);
-  const int b = sel[idx];
-  bool keep = geom_ok && b >= 0 && b < nb && b * kBlock <= last_q && doc_blk_off[d] + b < R;
-  if (keep) {
-    const int32_t* row = sel + (idx - s);
-    for (int s2 = 0; s2 < s; ++s2)
-      if (row[s2] == b) { keep = false; break; }
+  int32_t* counts = row_count + (int64_t)(blockIdx.x % kCounterCopies) * Hkv * R;
+  bool dropped_slot = false;
+  if (idx < total) {
+    const int s = (int)(idx % K);
+    const int g = (int)((idx / K) % C);
+    const int i = (int)(idx / ((int64_t)K * C));
+    const bool geom_ok = err[1] == 0;
+    int d = upper_bound_minus1(doc_chunk_off, num_docs + 1, g);
+    d = d < num_docs ? d : num_docs - 1;
+    const int c = g - doc_chunk_off[d];
+    const int len = cu[d + 1] - cu[d];
+    const int nb = (len + kBlock - 1) / kBlock;
+    const int last_q = min(kChunk * c + kChunk - 1, len - 1);
+    const int b = sel[idx];
+    bool keep = geom_ok && b >= 0 && b < nb && b * kBlock <= last_q && doc_blk_off[d] + b < R;
+    if (keep) {
+      const int32_t* row = sel + (idx - s);
+      for (int s2 = 0; s2 < s; ++s2)
+        if (row[s2] == b) { keep = false; break; }
+    }
+    sel_clean[idx] = keep ? b : -1;
+    if (i == 0 && s == 0) chunk_doc[g] = d;
+    if (keep) atomicAdd(&counts[(int64_t)i * R + doc_blk_off[d] + b], 1);
+    dropped_slot = b != -1 && !keep;
   }
-  sel_clean[idx] = keep ? b : -1;
-  if (i == 0 && s == 0) chunk_doc[g] = d;
-  if (keep) atomicAdd(&row_count[(int64_t)i * R + doc_blk_off[d] + b], 1);
-  if (b != -1 && !keep) atomicAdd(&err[0], 1);
+  // dropped slots: one atomic per workgroup (every thread reaches this barrier)
+  const int dropped = __syncthreads_count(dropped_slot);
+  if (threadIdx.x == 0 && dropped) atomicAdd(&err[0], dropped);
 }
 
 __global__ __launch_bounds__(kThreads) void scan_kernel(
@@ -129,18 +146,31 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(
   __shared__ int s_warp[kThreads / 64];
   const int tid = threadIdx.x;
   int n_total = 0;
+  const int64_t HR = (int64_t)Hkv * R;
   for (int i = 0; i < Hkv; ++i) {
     int32_t* cnt = row_cursor + (int64_t)i * R;
     int32_t* rp = row_ptr + (int64_t)i * (R + 1);
     int carry = 0;
     for (int base = 0; base < R; base += kThreads) {
       const int r = base + tid;
-      const int x = r < R ? cnt[r] : 0;
+      int part[kCounterCopies];
+      int x = 0;
+#pragma unroll
+      for (int cpy = 0; cpy < kCounterCopies; ++cpy) {
+        part[cpy] = r < R ? cnt[cpy * HR + r] : 0;
+        x += part[cpy];
+      }
       int tot;
       const int inc = block_inclusive_scan(x, s_warp, &tot);
       if (r < R) {
         rp[r + 1] = carry + inc;
-        cnt[r] = carry + inc - x;  // becomes the fill cursor
+        // the copies' fill cursors: consecutive sub-ranges of the row
+        int start = carry + inc - x;
+#pragma unroll
+        for (int cpy = 0; cpy < kCounterCopies; ++cpy) {
+          cnt[cpy * HR + r] = start;
+          start += part[cpy];
+        }
       }
       carry += tot;
     }
@@ -174,6 +204,7 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t cap1 = (int64_t)C * K;
   if (idx >= (int64_t)Hkv * cap1) return;
+  int32_t* cursor = row_cursor + (int64_t)(blockIdx.x % kCounterCopies) * Hkv * R;
   const int i = (int)(idx / cap1);
   const int64_t e = idx - (int64_t)i * cap1;
   const int g = (int)(e / K);
@@ -181,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(
   if (b >= 0) {
     const int d = chunk_doc[g];
     const int c = g - doc_chunk_off[d];
-    const int pos = atomicAdd(&row_cursor[(int64_t)i * R + doc_blk_off[d] + b], 1);
+    const int pos = atomicAdd(&cursor[(int64_t)i * R + doc_blk_off[d] + b], 1);
     q_idx[(int64_t)i * cap1 + pos] = kChunk * c;
   }
   if (e >= row_ptr[(int64_t)i * (R + 1) + R]) q_idx[idx] = -1;
@@ -249,10 +280,14 @@ hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const 
                                  int32_t* sched, const msa_schedule_layout& L, hipStream_t stream) {
   const int Hkv = p.num_kv_heads, C = p.num_chunks, K = p.topk, R = p.num_kblocks;
   const int64_t cap = (int64_t)Hkv * C * K;
-  hipLaunchKernelGGL(geometry_kernel, dim3(1), dim3(kThreads), 0, stream, cu, p.num_docs,
+  // clean and fill must use the same grid: a slot's counter copy is its
+  // workgroup id modulo kCounterCopies in both
+  const int64_t n_cursor = (int64_t)kCounterCopies * Hkv * R;
+  const unsigned zero_blocks = (unsigned)((n_cursor + kZeroPerBlock - 1) / kZeroPerBlock);
+  hipLaunchKernelGGL(geometry_kernel, dim3(1 + zero_blocks), dim3(kThreads), 0, stream, cu, p.num_docs,
                      p.total_tokens, C, R, p.max_doc_chunks, sched + L.doc_chunk_off,
                      sched + L.doc_blk_off, sched + L.desc, sched + L.err, sched + L.row_cursor,
-                     (int64_t)Hkv * R);
+                     n_cursor);
   const unsigned grid = (unsigned)((cap + kThreads - 1) / kThreads);
   if (cap > 0)
     hipLaunchKernelGGL(clean_kernel, dim3(grid), dim3(kThreads), 0, stream, cu, sel, Hkv, C, K, R,

@@ -99,7 +99,7 @@ typedef struct msa_problem {
  *   doc_chunk_off[num_docs+1], doc_blk_off[num_docs+1] : per-document offsets
  *   chunk_doc[C]          : document of each global chunk
  *   sel_clean[Hkv*C*topk] : kept ids in their slots, -1 elsewhere
- *   row_cursor[Hkv*R]     : build scratch
+ *   row_cursor[8*Hkv*R]   : build scratch (8 striped copies of the row counters)
  *   row_ptr[Hkv*(R+1)]    : k2q CSR offsets, one CSR per index head
  *   head_off[Hkv+1]       : first task row of each index head
  *   q_idx[Hkv*C*topk]     : CSR entries = document-local first query (8*c) of
