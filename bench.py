@@ -178,7 +178,28 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     per_kernel = {n: float(np.mean([events[s][j].elapsed_time(events[s][j + 1])
                                     for s in range(args.steps)])) for j, n in enumerate(names)}
+    per_kernel_median = {n: float(np.median([events[s][j].elapsed_time(events[s][j + 1])
+                                             for s in range(args.steps)])) for j, n in enumerate(names)}
     ms_step = elapsed * 1e3 / args.steps
+
+    # One cold step after a 512 MiB write has pushed the inputs out of the caches.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush.fill_(1)
+    cold = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    step(cold)
+    torch.cuda.synchronize()
+    cold_kernels = {n: cold[j].elapsed_time(cold[j + 1]) for j, n in enumerate(names)}
+    cold_ms = cold[0].elapsed_time(cold[6])
+    del flush
+
+    # Secondary count: only the unmasked (query, key) entries of each tile
+    # (the causal part of diagonal blocks and keys past a document end drop out).
+    tm = B.schedule_views(p, sched)["task_meta"][:n_pairs].cpu().numpy().astype(np.int64)
+    lens = np.diff(w.cu_seqlens.astype(np.int64))[tm[:, 4]]
+    pos = tm[:, 2:3] + np.arange(8)[None, :]                       # query positions of the chunk
+    valid_q = np.arange(8)[None, :] < tm[:, 3:4]
+    seen = np.clip(np.minimum(pos, lens[:, None] - 1) - w.block * tm[:, 5:6] + 1, 0, w.block)
+    unmasked_fraction = float((seen * valid_q).sum()) / (n_pairs * 8 * w.block) if n_pairs else 0.0
 
     fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
     gemm = bwd_f // 5
@@ -210,6 +231,13 @@ def main() -> int:
                    "selected_pairs": n_pairs, "num_cus": num_cus, "dq_mode": args.dq_mode},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(x, 4) for n, x in per_kernel.items()},
+        "kernels_ms_median": {n: round(x, 4) for n, x in per_kernel_median.items()},
+        "forward_plus_schedule_ms": round(per_kernel["schedule"] + per_kernel["forward"], 4),
+        "backward_ms": round(bwd_ms, 4),
+        "cold_step": {"ms": round(cold_ms, 4), "kernels_ms": {n: round(x, 4) for n, x in cold_kernels.items()},
+                      "note": "one step after writing a 512 MiB buffer"},
+        "unmasked_only": {"fraction_of_tile_entries": round(unmasked_fraction, 4),
+                          "value": round(value * unmasked_fraction, 3), "unit": "TFLOP/s"},
         "kernels_useful_tflops": {n: round(x, 2) for n, x in tflops.items()},
         "kernels_pct_peak": {n: round(100.0 * x / PEAK_BF16_TFLOPS, 2) for n, x in tflops.items()},
         "forward_pct_peak": round(100.0 * tflops["forward"] / PEAK_BF16_TFLOPS, 2),

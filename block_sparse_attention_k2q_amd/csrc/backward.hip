@@ -655,7 +655,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
         ds4[jg][rr] = (bf16)(pv * (dpt[j] - dl));
       }
       // P row of this query, keys 32kh + 8jg + 4h .. +3
-      store_bf16x4(pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), p4);
+      store_bf16x4(pd + swz8b_off(mq, 32 * kh + 8 * jg + 4 * h), p4);
     }
     if constexpr (WRITE_DS) {
       // A slot holds dS in the MFMA operand order of the dQ kernel: for each
@@ -688,7 +688,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       auto load_u = [&](int u, int slot) {
 #pragma unroll
         for (int x = 0; x < OUT_TILES; ++x)
-          ap[slot][x] = lds_tr_operand_swz<8>(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+          ap[slot][x] = lds_tr_operand_swz8b(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
                                               16 * u + 4, 16 * u + 12);
         bo[slot] = lds_tr_operand_swz<CPR>(T.dout, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
                                            16 * u + 12);
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     }
     lds_sync();      // every wave is done reading P
 #pragma unroll
-    for (int jg = 0; jg < 4; ++jg) store_bf16x4(pd + swz_off<8>(mq, 32 * kh + 8 * jg + 4 * h), ds4[jg]);
+    for (int jg = 0; jg < 4; ++jg) store_bf16x4(pd + swz8b_off(mq, 32 * kh + 8 * jg + 4 * h), ds4[jg]);
     lds_sync();      // dS complete
 
     // --- dK += dS^T Q over the 64 query rows of the half ------------------------
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       auto load_u = [&](int u, int slot) {
 #pragma unroll
         for (int x = 0; x < OUT_TILES; ++x)
-          ad[slot][x] = lds_tr_operand_swz<8>(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
+          ad[slot][x] = lds_tr_operand_swz8b(pd, 32 * own_mt[x], lane, 16 * u, 16 * u + 8,
                                               16 * u + 4, 16 * u + 12);
         bq[slot] = lds_tr_operand_swz<CPR>(T.q, 32 * nt, lane, 16 * u, 16 * u + 8, 16 * u + 4,
                                            16 * u + 12);

@@ -119,6 +119,28 @@ __device__ __forceinline__ bf16x8 lds_tr_operand_swz(const bf16* tile, int col0,
   return join_tr(lo, hi);
 }
 
+// 64-column bf16 tile (128-byte rows) swizzled in 8-byte slots: slot s of
+// row r is stored at slot s ^ p8(r).  Written 8 bytes per lane down 32
+// consecutive rows and read with the transpose load (4 rows x 4 slots per
+// 16 lanes), both patterns hit every LDS bank once per 32 lanes; a 16-byte
+// chunk swizzle leaves the column writes two-way conflicted.
+__device__ __forceinline__ int slot_swizzle8(int row) { return ((row >> 1) & 15) ^ ((row & 3) << 2); }
+__device__ __forceinline__ int swz8b_off(int row, int col) {
+  return row * 64 + (((col >> 2) ^ slot_swizzle8(row)) << 2) + (col & 3);
+}
+// Transposing operand from such a tile (same contract as lds_tr_operand).
+__device__ __forceinline__ bf16x8 lds_tr_operand_swz8b(const bf16* tile, int col0, int lane, int row_lo_h0,
+                                                       int row_lo_h1, int row_hi_h0, int row_hi_h1) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+  const int h = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * c;
+  const int rlo = (h ? row_lo_h1 : row_lo_h0) + r;
+  const int rhi = (h ? row_hi_h1 : row_hi_h0) + r;
+  shortx4 lo = lds_read_tr4(tile + swz8b_off(rlo, col));
+  shortx4 hi = lds_read_tr4(tile + swz8b_off(rhi, col));
+  return join_tr(lo, hi);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l of the wave writes
 // bytes [16 l, 16 l + 16) after lds_wave_base (wave-uniform).
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
