@@ -38,7 +38,8 @@ KERNEL_NAMES = {  # per dq mode
                   "bwd_dq": "dq_kernel<128>"},
     "ds": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true>",
            "bwd_dq": "dq_from_ds_kernel<128>"},
-    "atomic": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
+    "atomic": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, false>"},
+    "atomic_bf16": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
 }
 
 
@@ -113,7 +114,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dq-mode", choices=("ds", "recompute", "atomic"), default="ds")
+    ap.add_argument("--dq-mode", choices=("ds", "recompute", "atomic", "atomic_bf16"), default="ds")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run a plain device-to-device copy of this many MiB "
                          "three times (the known-size reference for HBM byte counters)")
@@ -132,7 +133,8 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     num_cus = B.msa_device_check(0)
     w = make_workload(WORKLOAD)
-    dq_mode = {"recompute": B.DQ_RECOMPUTE, "ds": B.DQ_DS_BUFFER, "atomic": B.DQ_ATOMIC_POOL}[args.dq_mode]
+    dq_mode = {"recompute": B.DQ_RECOMPUTE, "ds": B.DQ_DS_BUFFER, "atomic": B.DQ_ATOMIC_POOL,
+               "atomic_bf16": B.DQ_ATOMIC_POOL_BF16}[args.dq_mode]
     p = B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk, num_cus=num_cus,
                        softmax_scale=w.scale, block_size=w.block, dq_mode=dq_mode)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
@@ -205,8 +207,8 @@ def main() -> int:
     gemm = bwd_f // 5
     value = n_pairs * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     # useful contractions per pair done by each kernel
-    useful = {"forward": fwd_f, "bwd_main": (5 if dq_mode == B.DQ_ATOMIC_POOL else 4) * gemm,
-              "bwd_dq": (0 if dq_mode == B.DQ_ATOMIC_POOL else 1) * gemm}
+    pool = dq_mode in (B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16)
+    useful = {"forward": fwd_f, "bwd_main": (5 if pool else 4) * gemm, "bwd_dq": (0 if pool else 1) * gemm}
     tflops = {kname: n_pairs * f / (per_kernel[kname] * 1e-3) / 1e12 for kname, f in useful.items()
               if per_kernel[kname] > 0 and f > 0}
     bwd_ms = per_kernel["bwd_pre"] + per_kernel["bwd_main"] + per_kernel["bwd_dq"] + per_kernel["bwd_post"]

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_HIP = range(6)
 SCHED_ERR_DROPPED, SCHED_ERR_GEOMETRY = 0, 1
-DQ_RECOMPUTE, DQ_ATOMIC_POOL, DQ_DS_BUFFER = 0, 1, 2
+DQ_RECOMPUTE, DQ_ATOMIC_POOL, DQ_DS_BUFFER, DQ_ATOMIC_POOL_BF16 = 0, 1, 2, 3
 MAX_DOC_CHUNKS = 1 << 18
 
 EXPORTED = (

@@ -41,7 +41,7 @@ int check_problem(const msa_problem* p) {
     return MSA_ERR_SHAPE;
   if (!(p->softmax_scale > 0.f)) return MSA_ERR_INVALID;
   if (p->dq_mode != MSA_DQ_RECOMPUTE && p->dq_mode != MSA_DQ_ATOMIC_POOL &&
-      p->dq_mode != MSA_DQ_DS_BUFFER)
+      p->dq_mode != MSA_DQ_DS_BUFFER && p->dq_mode != MSA_DQ_ATOMIC_POOL_BF16)
     return MSA_ERR_INVALID;
   return MSA_OK;
 }

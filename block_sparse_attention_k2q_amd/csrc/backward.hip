@@ -36,7 +36,8 @@ constexpr int kBwdThreads = 256;
 constexpr int kMaxWalk = 64;   // ROWS_PER_CTA_LARGE: longest walk a workgroup takes
 
 // ---------------------------------------------------------------------------
-// Preprocess: Delta = rowsum(dO * O) in fp32; zero the dQ pool and dK/dV.
+// Preprocess: Delta = rowsum(dO * O) in fp32; zero the dQ pool (fp32 or bf16)
+// and dK/dV.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(const bf16* __restrict__ out,
@@ -61,10 +62,12 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const bf16* __restrict_
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off, 64);
   if ((x % LPR) == 0) delta[x / LPR] = s;
-  if (zero_pool) {
+  if (zero_pool == 1) {          // fp32 pool: 8 floats per vector
     floatx4* p = reinterpret_cast<floatx4*>(dq_pool) + 2 * x;
     p[0] = floatx4{};
     p[1] = floatx4{};
+  } else if (zero_pool == 2) {   // bf16 pool: 8 bf16 per vector
+    reinterpret_cast<floatx4*>(dq_pool)[x] = floatx4{};
   }
 }
 
@@ -96,6 +99,28 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
   }
 }
 
+// dq from the head-pair-interleaved bf16 pool (already scaled): thread x
+// writes dq elements 8x .. 8x+7 = (token, head h, d0 .. d0+7).
+template <int D>
+__global__ __launch_bounds__(256) void pool_bf16_to_dq_kernel(const bf16* __restrict__ pool,
+                                                              bf16* __restrict__ dq, int64_t n_q_vec) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n_q_vec) return;
+  const int64_t e = 8 * x;
+  const int d0 = (int)(e % D);
+  const int64_t th = e / D;                 // token * Hq + h
+  const int64_t pair = th >> 1, odd = th & 1;
+  const bf16x8 a = load_bf16x8(pool + (pair * D + d0) * 2);
+  const bf16x8 b = load_bf16x8(pool + (pair * D + d0) * 2 + 8);
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[k] = a[2 * k + odd];
+    r[4 + k] = b[2 * k + odd];
+  }
+  store_bf16x8(dq + e, r);
+}
+
 // ---------------------------------------------------------------------------
 // Main kernel.
 // ---------------------------------------------------------------------------
@@ -114,12 +139,12 @@ struct BwdSmem {
   int meta[kMaxWalk][8];   // per walked task: i, r, qb, qc, d, b, tok0, len
 };
 
-template <int D, bool ATOMIC_DQ>
+template <int D, bool BF16_POOL>
 __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
-    const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dq_pool,
+    const int32_t* __restrict__ desc, const int32_t* __restrict__ err, void* __restrict__ dq_pool,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, int Hkv, float scale) {
   using S = BwdSmem<D>;
   constexpr int LDK = S::LDK, LDP = S::LDP;
@@ -332,8 +357,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
       }
     }
 
-    // --- dQ = dS K (32 query rows x D) -> fp32 pool (atomic-pool mode) --------
-    if constexpr (ATOMIC_DQ) {
+    // --- dQ = dS K (32 query rows x D) -> dQ pool ------------------------------
+    {
       floatx16 dq[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) dq[t] = floatx16{};
@@ -356,14 +381,34 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
       // dS are 0); they are sent to the tile's first row, which always exists,
       // so the atomics need no branch.
       const int64_t row0 = (int64_t)(tok0 + qb) * Hq + kQPerKV * i;
+      if constexpr (BF16_POOL) {
+        // Registers j and j+1 (j even) hold heads hh and hh+1 of one token:
+        // one packed atomic adds both, pre-scaled, into the interleaved pool.
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const int64_t pair0 = row0 >> 1;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
-        const int jt = m >> 4, hh = m & 15;
-        const int64_t rowm = jt < qc ? row0 + (int64_t)jt * Hq + hh : row0;
-        float* dst = dq_pool + rowm * D + n32;
+        for (int j = 0; j < 16; j += 2) {
+          const int m = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+          const int jt = m >> 4, hh = m & 15;
+          const int64_t pr = jt < qc ? pair0 + (int64_t)jt * (Hq / 2) + (hh >> 1) : pair0;
+          bf16x2* dst = reinterpret_cast<bf16x2*>(dq_pool) + pr * D + n32;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) atomicAdd(dst + 32 * t, dq[t][j]);
+          for (int t = 0; t < NT; ++t) {
+            const bf16x2 val = {(bf16)(dq[t][j] * scale), (bf16)(dq[t][j + 1] * scale)};
+            __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                (__attribute__((address_space(1))) bf16x2*)(dst + 32 * t), val);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+          const int jt = m >> 4, hh = m & 15;
+          const int64_t rowm = jt < qc ? row0 + (int64_t)jt * Hq + hh : row0;
+          float* dst = reinterpret_cast<float*>(dq_pool) + rowm * D + n32;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) atomicAdd(dst + 32 * t, dq[t][j]);
+        }
       }
     }
     lds_barrier();  // P, dS complete in LDS
@@ -754,7 +799,8 @@ hipError_t launch_backward_preprocess(const msa_problem& p, const void* out, con
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, (const bf16*)out, (const bf16*)dout,
                        (float*)(base + L.delta), (float*)(base + L.dq_pool), (float*)(base + L.dk_acc),
-                       n_vec, n_dkv_vec, p.dq_mode == MSA_DQ_ATOMIC_POOL ? 1 : 0);
+                       n_vec, n_dkv_vec,
+                       p.dq_mode == MSA_DQ_ATOMIC_POOL ? 1 : p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16 ? 2 : 0);
   };
   if (p.head_dim == 128) go(preprocess_kernel<128>);
   else go(preprocess_kernel<64>);
@@ -776,11 +822,15 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), lds, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
-                       sched + L.err, (float*)(base + S.dq_pool), (float*)(base + S.dk_acc),
+                       sched + L.err, (void*)(base + S.dq_pool), (float*)(base + S.dk_acc),
                        (float*)(base + S.dv_acc), p.num_kv_heads, p.softmax_scale);
     return hipGetLastError();
   };
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) {
+    if (p.head_dim == 128) return go(backward_main_kernel<128, false>, sizeof(BwdSmem<128>));
+    return go(backward_main_kernel<64, false>, sizeof(BwdSmem<64>));
+  }
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) {
     if (p.head_dim == 128) return go(backward_main_kernel<128, true>, sizeof(BwdSmem<128>));
     return go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>));
   }
@@ -816,6 +866,17 @@ hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch
                      (const float*)(base + L.dq_pool), (const float*)(base + L.dk_acc),
                      (const float*)(base + L.dv_acc), (bf16*)dq, (bf16*)dk, (bf16*)dv, n_q_vec, n_kv_vec,
                      p.softmax_scale);
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) {
+    const int64_t n_pool_vec = (int64_t)p.total_tokens * hq * p.head_dim / 8;
+    if (n_pool_vec > 0) {
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)((n_pool_vec + 255) / 256)), dim3(256), 0, stream,
+                           (const bf16*)(base + L.dq_pool), (bf16*)dq, n_pool_vec);
+      };
+      if (p.head_dim == 128) go(pool_bf16_to_dq_kernel<128>);
+      else go(pool_bf16_to_dq_kernel<64>);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -302,7 +302,7 @@ hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k
                               const void* dout, const float* lse, const int32_t* cu,
                               const int32_t* sched, const msa_schedule_layout& L, const void* scratch,
                               void* dq, hipStream_t stream) {
-  if (p.dq_mode == MSA_DQ_ATOMIC_POOL) return hipSuccess;
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL || p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) return hipSuccess;
   const int64_t nwg = (int64_t)p.num_chunks * p.num_kv_heads;
   if (nwg == 0) return hipSuccess;
   const BackwardScratch S = backward_scratch_layout(p);

@@ -69,6 +69,7 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   s.dv_acc = o; o = a256(o + 4 * T * hkv * D);
   s.dq_pool = o;
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) o = a256(o + 4 * T * hq * D);
+  if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) o = a256(o + 2 * T * hq * D);
   s.ds = o;
   if (p.dq_mode == MSA_DQ_DS_BUFFER)
     o = a256(o + (size_t)kDsSlotBytes * hkv * (size_t)p.num_chunks * (size_t)p.topk);

@@ -65,7 +65,8 @@ typedef struct msa_problem {
   int32_t max_doc_chunks;  /* max_d ceil(len_d / 8); <= MSA_MAX_DOC_CHUNKS */
   int32_t num_cus;         /* compute units the walk is sized for (msa_device_check) */
   float softmax_scale;     /* usually head_dim ** -0.5 (msa_schedule: SOFTMAX_SCALE) */
-  int32_t dq_mode;         /* MSA_DQ_RECOMPUTE, MSA_DQ_ATOMIC_POOL or MSA_DQ_DS_BUFFER */
+  int32_t dq_mode;         /* MSA_DQ_DS_BUFFER, MSA_DQ_RECOMPUTE, MSA_DQ_ATOMIC_POOL or
+                              MSA_DQ_ATOMIC_POOL_BF16 */
 } msa_problem;
 
 /* How the backward forms dQ.
@@ -86,6 +87,13 @@ typedef struct msa_problem {
 #define MSA_DQ_RECOMPUTE 0
 #define MSA_DQ_ATOMIC_POOL 1
 #define MSA_DQ_DS_BUFFER 2
+/* MSA_DQ_ATOMIC_POOL_BF16: the pages' pool dtype (msa_schedule page:
+ *   DQ_ACCUM_DTYPE bf16; msa_backward_sm100 page: head-pair-interleaved bf16x2
+ *   atomics).  The pool is bf16 [T, Hq/2, D, 2]: element (t, h, d) at
+ *   ((t * Hq/2 + h/2) * D + d) * 2 + h%2, so one packed atomic adds the dQ of
+ *   two heads; each tile's scale * dQ is rounded to bf16 and summed in bf16
+ *   (less accurate than the fp32 pool; half its atomic operations). */
+#define MSA_DQ_ATOMIC_POOL_BF16 3
 
 #define MSA_MAX_DOC_CHUNKS (1 << 18) /* documents up to 2 Mi tokens (32 KiB LDS bitmap per bucket sort) */
 
@@ -145,7 +153,8 @@ int msa_forward(const msa_problem* p, const void* q, const void* k, const void* 
 /* Bytes of scratch msa_backward needs: fp32 Delta [T, Hq], fp32 dK and dV
  * accumulators [T, Hkv, D]; in MSA_DQ_ATOMIC_POOL mode the fp32 dQ pool
  * [T, Hq, D]; in MSA_DQ_DS_BUFFER mode the bf16 dS slots
- * [Hkv, C, topk, 128, 64] (16 KiB per slot). */
+ * [Hkv, C, topk, 128, 64] (16 KiB per slot); in MSA_DQ_ATOMIC_POOL_BF16 mode
+ * the bf16 pool [T, Hq/2, D, 2]. */
 int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
 
 /* KV-parallel backward (msa_backward_sm100: run_backward): preprocess
@@ -163,9 +172,8 @@ int msa_backward(const msa_problem* p, const void* q, const void* k, const void*
 
 /* The steps of msa_backward, callable one at a time (same arguments and
  * scratch; used to time each kernel).  Order: preprocess, main, dq,
- * postprocess.  msa_backward_dq writes dq directly and does nothing in
- * MSA_DQ_ATOMIC_POOL mode; msa_backward_postprocess writes dq only in that
- * mode. */
+ * postprocess.  msa_backward_dq writes dq directly and does nothing in the
+ * two pool modes; msa_backward_postprocess writes dq only in those modes. */
 int msa_backward_preprocess(const msa_problem* p, const void* out, const void* dout,
                             void* scratch, void* stream);
 int msa_backward_main(const msa_problem* p, const void* q, const void* k, const void* v,

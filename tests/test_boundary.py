@@ -46,6 +46,8 @@ def test_schedule_layout_is_host_only_and_sized():
     assert base <= B.msa_backward_scratch_bytes(p) < base + 4096
     pa = B.Problem(**{**p.__dict__, "dq_mode": B.DQ_ATOMIC_POOL})
     assert B.msa_backward_scratch_bytes(pa) >= base + 4 * 8192 * 64 * 128   # plus the fp32 dQ pool
+    pb = B.Problem(**{**p.__dict__, "dq_mode": B.DQ_ATOMIC_POOL_BF16})
+    assert base + 2 * 8192 * 64 * 128 <= B.msa_backward_scratch_bytes(pb) < base + 2 * 8192 * 64 * 128 + 4096
     pd = B.Problem(**{**p.__dict__, "dq_mode": B.DQ_DS_BUFFER})
     slots = 4 * 1024 * 16
     assert base + slots * 128 * 64 * 2 <= B.msa_backward_scratch_bytes(pd) < base + slots * 128 * 64 * 2 + 4096
@@ -59,7 +61,7 @@ def test_schedule_layout_is_host_only_and_sized():
     ("num_chunks", 5, ValueError),
     ("num_docs", 0, ValueError),
     ("softmax_scale", 0.0, ValueError),
-    ("dq_mode", 3, ValueError),
+    ("dq_mode", 4, ValueError),
 ])
 def test_bad_problems_are_rejected_on_the_host(field, value, exc):
     good = B.Problem.make([0, 512], 1, 64, 4)

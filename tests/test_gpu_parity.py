@@ -73,7 +73,8 @@ SMALL["empty_chunks"] = _empty_rows_workload
 @pytest.mark.parametrize("case", list(SMALL))
 @pytest.mark.parametrize("num_cus,dq_mode", [(None, B.DQ_RECOMPUTE), (7, B.DQ_RECOMPUTE),
                                              (None, B.DQ_ATOMIC_POOL), (7, B.DQ_ATOMIC_POOL),
-                                             (None, B.DQ_DS_BUFFER), (7, B.DQ_DS_BUFFER)])
+                                             (None, B.DQ_DS_BUFFER), (7, B.DQ_DS_BUFFER),
+                                             (None, B.DQ_ATOMIC_POOL_BF16), (7, B.DQ_ATOMIC_POOL_BF16)])
 def test_small_cases_full_parity(case, num_cus, dq_mode):
     w = SMALL[case]()
     print(f"[case] {case} num_cus={num_cus} dq_mode={dq_mode} T={w.total_tokens} "
@@ -103,7 +104,8 @@ FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
 
 
 @pytest.mark.parametrize("name,dq_mode", [(n, B.DQ_RECOMPUTE) for n in FULL] +
-                         [(n, B.DQ_DS_BUFFER) for n in FULL] + [("single8k", B.DQ_ATOMIC_POOL)])
+                         [(n, B.DQ_DS_BUFFER) for n in FULL] + [("single8k", B.DQ_ATOMIC_POOL),
+                                                                ("single8k", B.DQ_ATOMIC_POOL_BF16)])
 def test_full_size_configs_sampled(name, dq_mode):
     print(f"[case] full-size {name} dq_mode={dq_mode}", flush=True)
     w = make_workload(name)
