@@ -5,20 +5,22 @@
 // forward's bf16 out [T, Hq, D] and fp32 lse [T, Hq]).  The kernel below is
 // this library's own design for CDNA4:
 //
-//  * one workgroup of 2 waves per (chunk, index head): a 128-row query tile
-//    of 8 tokens x 16 query heads sharing one KV head, each wave owning 64
-//    rows (two 32-query MFMA columns).  Workgroup ids run head-fastest, so
+//  * one workgroup of 4 waves per (chunk, index head): a 128-row query tile
+//    of 8 tokens x 16 query heads sharing one KV head, each wave owning one
+//    32-query MFMA column (2 tokens).  Workgroup ids run head-fastest, so
 //    with 4 or 8 KV heads each XCD (ids are dealt to the 8 XCDs round-robin)
 //    reads the K/V of one head only, which then stays in its L2;
 //  * the tile's Q rows live in registers as MFMA B operands for the whole
 //    chunk;
 //  * per kept key block (64 keys): K and V arrive in LDS by direct
-//    global->LDS loads into one of two swizzled buffers, the next block's
-//    copy in flight while the current one is consumed (one barrier per
-//    block);  S^T = K Q^T (keys x queries, so a lane owns one query column),
-//    online softmax in the exp2 domain with the causal mask, and
-//    O^T += V^T P^T with P^T taken straight from the S^T accumulators and V^T
-//    read by the LDS transpose load;
+//    global->LDS loads into a K ring of three and a V ring of two swizzled
+//    buffers (80 KiB at D = 128, two workgroups per CU), so K of block j+2
+//    and V of block j+1 are in flight while block j is consumed, with one
+//    barrier per block;  S^T = K Q^T (keys x queries, so a lane owns one
+//    query column), online softmax in the exp2 domain with the causal mask
+//    and a lazy rescale (O is rescaled only when the running max grows by
+//    more than 2^8), and O^T += V^T P^T with P^T taken straight from the S^T
+//    accumulators and V^T read by the LDS transpose load;
 //  * out = O / l in bf16, lse = ln(sum exp(scale * s)) in fp32.
 #include "msa_device.h"
 #include "msa_internal.h"
