@@ -26,16 +26,20 @@ int check_problem(const msa_problem* p) {
   if (p->total_tokens < 0 || p->num_docs < 1 || p->num_kv_heads < 1 || p->topk < 1 ||
       p->num_chunks < 0 || p->num_kblocks < 0 || p->max_doc_chunks < 0 || p->num_cus < 1)
     return MSA_ERR_INVALID;
-  if (p->q_per_kv != 16 || p->block_size != 64 || p->query_chunk != 8 ||
+  if (p->q_per_kv != 16 || (p->block_size != 64 && p->block_size != 128) || p->query_chunk != 8 ||
       (p->head_dim != 64 && p->head_dim != 128) || p->topk > 64 ||
       p->max_doc_chunks > MSA_MAX_DOC_CHUNKS)
+    return MSA_ERR_UNSUPPORTED;
+  // Key block 128 runs as two 64-key halves: at most 64 halves per
+  // selection row, and dQ from the stored dS only.
+  if (p->block_size == 128 && (p->topk > 32 || p->dq_mode != MSA_DQ_DS_BUFFER))
     return MSA_ERR_UNSUPPORTED;
   // Size limits so every flat index fits the 32/64-bit arithmetic the kernels use.
   const int64_t cap = (int64_t)p->num_kv_heads * p->num_chunks * p->topk;
   if (cap > (int64_t)INT32_MAX / 6 || (int64_t)p->num_kv_heads * (p->num_kblocks + 1) > INT32_MAX)
     return MSA_ERR_UNSUPPORTED;
   // Geometry implied by the sizes themselves.
-  if ((int64_t)p->num_chunks * 8 < p->total_tokens || (int64_t)p->num_kblocks * 64 < p->total_tokens ||
+  if ((int64_t)p->num_chunks * 8 < p->total_tokens || (int64_t)p->num_kblocks * p->block_size < p->total_tokens ||
       p->num_chunks > p->total_tokens || p->num_kblocks > p->num_chunks ||
       p->max_doc_chunks > p->num_chunks || (p->num_chunks > 0 && p->max_doc_chunks < 1))
     return MSA_ERR_SHAPE;

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dk_acc,
     float* __restrict__ dv_acc, bf16* __restrict__ ds, const int32_t* __restrict__ doc_chunk_off,
-    const int32_t* __restrict__ sel_clean, int Hkv, int C, int K, float scale) {
+    const int32_t* __restrict__ sel_clean, int Hkv, int C, int K, int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -525,8 +525,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
 
   if (err[1]) return;
   const int grid_walks = desc[5];
-  const int wg = blockIdx.x >> 1;
-  const int half = blockIdx.x & 1;
+  // Key block 128 (sub = 2): workgroups x and x + 8 (same XCD, launched
+  // close together) take the two 64-key tiles of the same walk half, so
+  // the second gathers its Q / dO rows from the L2.
+  const int tsub = sub == 1 ? 0 : (blockIdx.x >> 3) & 1;
+  const int unit = sub == 1 ? blockIdx.x : ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
+  const int wg = unit >> 1;
+  const int half = unit & 1;
   if (wg >= grid_walks) return;
   const int rpc = desc[1], full = desc[2], tail = desc[3], tail_walks = desc[4];
   int lo, hi;
@@ -588,18 +593,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     int* m = meta[e];
 #pragma unroll
     for (int x = 0; x < 6; ++x) m[x] = tm[x];
+    m[5] = sub * tm[5] + tsub;   // this workgroup's 64-key tile of the block
     const int d = tm[4];
     const int t0 = cu[d];
     m[6] = t0;
     m[7] = cu[d + 1] - t0;
     if constexpr (WRITE_DS) {
-      // dS slot of the task: (index head, global chunk, position of its block
-      // in the chunk's cleaned selection); the document id is not needed later.
+      // dS slot of the tile: (index head, global chunk, position of its block
+      // in the chunk's cleaned selection, tile); the document id is not
+      // needed later.
       const int64_t row = (int64_t)tm[0] * C + doc_chunk_off[d] + tm[2] / kChunk;
       const int32_t* sel = sel_clean + row * K;
       int slot = -1;
       for (int x = 0; x < K; ++x) slot = sel[x] == tm[5] ? x : slot;
-      m[4] = slot < 0 ? -1 : (int)(row * K + slot);
+      m[4] = slot < 0 ? -1 : (int)((row * K + slot) * sub + tsub);
     }
   }
   lds_barrier();
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     lds_barrier();   // task e landed; every wave is done with task e-1 and with pd
 
     if (i != cur_i || r != cur_r) {
-      if (cur_i >= 0) flush();
+      if (cur_i >= 0 && cur_b * kBlock < cur_len) flush();   // a tile past the end holds no key
 #pragma unroll
       for (int x = 0; x < OUT_TILES; ++x) {
         acc_dv[x] = floatx16{};
@@ -653,7 +660,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       next_lse = lse[row_index(meta[e + 1])];
       next_delta = delta[row_index(meta[e + 1])];
     }
-    if (4 * half >= qc) return;   // this half holds no token of the chunk
+    // this half holds no token of the chunk, or the tile starts after the
+    // chunk's last query (second tile of a 128-key block: all keys masked)
+    if (4 * half >= qc || b * kBlock > qb + qc - 1) return;
 
     // --- S^T and dP^T: 32 keys x 32 queries per wave ---------------------------
     floatx16 st = floatx16{}, dpt = floatx16{};
@@ -780,7 +789,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     step(row, tile0, tile1);
     if (row + 1 < hi) step(row + 1, tile1, tile0);
   }
-  if (cur_i >= 0) flush();
+  if (cur_i >= 0 && cur_b * kBlock < cur_len) flush();
 }
 
 }  // namespace
@@ -836,12 +845,13 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
   }
   // Two workgroups per walk, one per query half of every task tile.
   auto go_kv = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads), 0, stream, (const bf16*)q,
+    const int sub = p.block_size / kBlock;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * sub * grid)), dim3(kBwdThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
                        (bf16*)(base + S.ds), sched + L.doc_chunk_off, sched + L.sel_clean,
-                       p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
+                       p.num_kv_heads, p.num_chunks, p.topk, sub, p.softmax_scale);
     return hipGetLastError();
   };
   if (p.dq_mode == MSA_DQ_DS_BUFFER) {

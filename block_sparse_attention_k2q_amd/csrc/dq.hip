@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ ds, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_doc, const int32_t* __restrict__ doc_chunk_off,
     const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ dq,
-    int Hkv, int C, int K, float scale) {
+    int Hkv, int C, int K, int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int NT = D / 32;
   constexpr int NW = kDqThreads / 64;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
   const int64_t row_base = ((int64_t)i * C + g) * K;
 
   if (threadIdx.x < 64) {
-    const int n = compact_selection(sel_clean + row_base, K, threadIdx.x, s_block, s_slot);
+    const int n = compact_tiles(sel_clean + row_base, K, sub, p0 + qcount - 1, threadIdx.x, s_block, s_slot);
     if (threadIdx.x == 0) s_n = n;
   }
 
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
   const bool qvalid = jq < qcount;
   const int64_t qrow = (int64_t)(tok0 + p0 + min(jq, qcount - 1)) * Hq + kQPerKV * i + (n32 & 15);
   // this lane's dS^T operand of step u: 8 bf16 at ((4w + u) * 64 + lane) * 8 in a slot
-  const bf16* ds_lane = ds + row_base * (kDsSlotBytes / 2) + w * 4 * 512 + lane * 8;
+  const bf16* ds_lane = ds + row_base * sub * (kDsSlotBytes / 2) + w * 4 * 512 + lane * 8;
 
   floatx16 acc[NT];
 #pragma unroll
@@ -311,7 +311,7 @@ hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k
       hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)k,
                          (const bf16*)((const uint8_t*)scratch + S.ds), cu, sched + L.chunk_doc,
                          sched + L.doc_chunk_off, sched + L.sel_clean, sched + L.err, (bf16*)dq,
-                         p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
+                         p.num_kv_heads, p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
     };
     if (p.head_dim == 128) go_ds(dq_from_ds_kernel<128>);
     else go_ds(dq_from_ds_kernel<64>);

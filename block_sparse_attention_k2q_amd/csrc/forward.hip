@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
     const int32_t* __restrict__ err, bf16* __restrict__ out, float* __restrict__ lse, int Hkv, int C,
-    int K, float scale) {
+    int K, int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
   constexpr int NT = D / 32;           // 32-wide d tiles of O^T
@@ -77,9 +77,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
   const int w = wave_id(), lane = lane_id();
   const int n32 = lane & 31, h = lane >> 5;
 
-  // Every wave reads the selection row itself: lane s holds slot s, the
-  // kept slots form a wave-uniform mask walked in slot order.
-  const int bsel = lane < K ? sel_clean[((int64_t)i * C + g) * K + lane] : -1;
+  // Every wave reads the selection row itself: lane s holds 64-key tile s of
+  // the row (slot s with key block 64; half s % 2 of slot s / 2 with key
+  // block 128), the kept tiles form a wave-uniform mask walked in order.
+  const int bsel = sub_tile(sel_clean + ((int64_t)i * C + g) * K, K, sub, p0 + qcount - 1, lane);
   const uint64_t kept = __builtin_amdgcn_ballot_w64(bsel >= 0);
   const int nblk = __popcll(kept);
   uint64_t rem_k = kept, rem_v = kept, rem_c = kept;
@@ -240,7 +241,7 @@ hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, co
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(threads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, cu, sched + L.chunk_doc, sched + L.doc_chunk_off,
                        sched + L.sel_clean, sched + L.err, (bf16*)out, lse, p.num_kv_heads,
-                       p.num_chunks, p.topk, p.softmax_scale);
+                       p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
   };
   if (p.head_dim == 128) args(forward_kernel<128>, kFwdThreads);
   else args(forward_kernel<64>, kFwdThreads);

@@ -330,6 +330,36 @@ __device__ __forceinline__ int compact_selection(const int32_t* __restrict__ row
   return __popcll(mask);
 }
 
+// Kernel tiles hold kBlock = 64 keys; a selected block of `sub` * 64 keys
+// (key block 128: sub = 2) is taken as `sub` consecutive 64-key tiles.
+// Lane s < sub * K stands for tile `sub * row[s / sub] + s % sub` of slot
+// s / sub.  A tile is kept when its slot is kept and its first key is not
+// after the chunk's last query `last_q` (later tiles hold only masked keys;
+// with sub = 1 every kept slot passes).  Returns the tile id or -1.
+__device__ __forceinline__ int sub_tile(const int32_t* __restrict__ row, int K, int sub, int last_q,
+                                        int lane) {
+  if (lane >= sub * K) return -1;
+  const int slot = sub == 1 ? lane : lane >> 1;
+  const int b = row[slot];
+  const int t = sub * b + (lane - sub * slot);
+  return b >= 0 && t * kBlock <= last_q ? t : -1;
+}
+
+// Kept tiles of a selection row compacted in lane order: blocks[n] = tile
+// id, slots[n] = its position sub * slot + s % sub in the row's tile list.
+__device__ __forceinline__ int compact_tiles(const int32_t* __restrict__ row, int K, int sub, int last_q,
+                                             int lane, int* blocks, int* slots) {
+  const int t = sub_tile(row, K, sub, last_q, lane);
+  const bool keep = t >= 0;
+  const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
+  const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+  if (keep) {
+    blocks[pos] = t;
+    slots[pos] = lane;
+  }
+  return __popcll(mask);
+}
+
 // Register-staged copy of key block b (K and V rows of KV head i) into
 // swizzled kBlock x D tiles (same piece layout and end-of-document rule as
 // stage_block): load_k() / load_v() issue plain 16-byte global loads into

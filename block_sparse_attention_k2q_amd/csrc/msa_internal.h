@@ -19,7 +19,8 @@ constexpr int kRowsPerWalkSwitch = 2400;
 // workgroup id) and the scan adds them up.
 constexpr int kCounterCopies = 8;
 
-// One dS slot of the MSA_DQ_DS_BUFFER mode: 128 tile rows x 64 keys, bf16.
+// One dS slot of the MSA_DQ_DS_BUFFER mode: 128 tile rows x 64 keys, bf16
+// (a selected block of 128 keys takes two).
 constexpr int kDsSlotBytes = 128 * 64 * 2;
 
 inline int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
@@ -72,7 +73,7 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) o = a256(o + 2 * T * hq * D);
   s.ds = o;
   if (p.dq_mode == MSA_DQ_DS_BUFFER)
-    o = a256(o + (size_t)kDsSlotBytes * hkv * (size_t)p.num_chunks * (size_t)p.topk);
+    o = a256(o + (size_t)kDsSlotBytes * hkv * (size_t)p.num_chunks * (size_t)p.topk * (size_t)(p.block_size / 64));
   s.total = o;
   return s;
 }

@@ -58,7 +58,7 @@ __device__ int block_inclusive_scan(int x, int* s_warp, int* total) {
 constexpr int kZeroPerBlock = 16 * kThreads;   // counters cleared per extra workgroup
 
 __global__ __launch_bounds__(kThreads) void geometry_kernel(
-    const int32_t* __restrict__ cu, int num_docs, int T, int C, int R, int max_doc_chunks,
+    const int32_t* __restrict__ cu, int num_docs, int T, int C, int R, int B, int max_doc_chunks,
     int32_t* __restrict__ doc_chunk_off, int32_t* __restrict__ doc_blk_off, int32_t* __restrict__ desc,
     int32_t* __restrict__ err, int32_t* __restrict__ row_cursor, int64_t n_cursor) {
   __shared__ int s_warp[kThreads / 64];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void geometry_kernel(
       if (len < 0 || a < 0) bad = 1;
       len = len < 0 ? 0 : len;
       nc = (len + kChunk - 1) / kChunk;
-      nb = (len + kBlock - 1) / kBlock;
+      nb = (len + B - 1) / B;
       if (nc > max_doc_chunks) bad = 1;
     }
     int tc, tb;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void geometry_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void clean_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ sel, int Hkv, int C, int K, int R,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ sel, int Hkv, int C, int K, int R, int B,
     int num_docs, const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_blk_off,
     int32_t* __restrict__ chunk_doc, int32_t* __restrict__ sel_clean, int32_t* __restrict__ row_count,
     int32_t* __restrict__ err) {
@@ -121,10 +121,10 @@ __global__ __launch_bounds__(kThreads) void clean_kernel(
     d = d < num_docs ? d : num_docs - 1;
     const int c = g - doc_chunk_off[d];
     const int len = cu[d + 1] - cu[d];
-    const int nb = (len + kBlock - 1) / kBlock;
+    const int nb = (len + B - 1) / B;
     const int last_q = min(kChunk * c + kChunk - 1, len - 1);
     const int b = sel[idx];
-    bool keep = geom_ok && b >= 0 && b < nb && b * kBlock <= last_q && doc_blk_off[d] + b < R;
+    bool keep = geom_ok && b >= 0 && b < nb && b * B <= last_q && doc_blk_off[d] + b < R;
     if (keep) {
       const int32_t* row = sel + (idx - s);
       for (int s2 = 0; s2 < s; ++s2)
@@ -285,12 +285,12 @@ hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const 
   const int64_t n_cursor = (int64_t)kCounterCopies * Hkv * R;
   const unsigned zero_blocks = (unsigned)((n_cursor + kZeroPerBlock - 1) / kZeroPerBlock);
   hipLaunchKernelGGL(geometry_kernel, dim3(1 + zero_blocks), dim3(kThreads), 0, stream, cu, p.num_docs,
-                     p.total_tokens, C, R, p.max_doc_chunks, sched + L.doc_chunk_off,
+                     p.total_tokens, C, R, p.block_size, p.max_doc_chunks, sched + L.doc_chunk_off,
                      sched + L.doc_blk_off, sched + L.desc, sched + L.err, sched + L.row_cursor,
                      n_cursor);
   const unsigned grid = (unsigned)((cap + kThreads - 1) / kThreads);
   if (cap > 0)
-    hipLaunchKernelGGL(clean_kernel, dim3(grid), dim3(kThreads), 0, stream, cu, sel, Hkv, C, K, R,
+    hipLaunchKernelGGL(clean_kernel, dim3(grid), dim3(kThreads), 0, stream, cu, sel, Hkv, C, K, R, p.block_size,
                        p.num_docs, sched + L.doc_chunk_off, sched + L.doc_blk_off, sched + L.chunk_doc,
                        sched + L.sel_clean, sched + L.row_cursor, sched + L.err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, stream, Hkv, R, cap, p.num_cus,

@@ -56,7 +56,7 @@ def test_schedule_layout_is_host_only_and_sized():
 @pytest.mark.parametrize("field,value,exc", [
     ("head_dim", 96, NotImplementedError),
     ("q_per_kv", 8, NotImplementedError),
-    ("block_size", 128, NotImplementedError),
+    ("block_size", 96, NotImplementedError),
     ("topk", 65, NotImplementedError),
     ("num_chunks", 5, ValueError),
     ("num_docs", 0, ValueError),
@@ -68,6 +68,24 @@ def test_bad_problems_are_rejected_on_the_host(field, value, exc):
     bad = B.Problem(**{**good.__dict__, field: value})
     with pytest.raises(exc):
         B.msa_schedule_layout_of(bad)
+
+
+def test_key_block_128_rules():
+    """Key block 128 runs as two 64-key tiles: topk <= 32, dQ from stored dS
+    only, and twice the dS slots of key block 64 at the same topk."""
+    p = B.Problem.make([0, 8192], 4, 128, 16, block_size=128, dq_mode=B.DQ_DS_BUFFER)
+    assert p.num_kblocks == 64
+    L = B.msa_schedule_layout_of(p)
+    assert L.task_meta + 6 * 4 * 1024 * 16 <= L.total
+    base = 4 * 8192 * 64 + 2 * 4 * 8192 * 4 * 128
+    slots = 4 * 1024 * 16 * 2
+    assert base + slots * 128 * 64 * 2 <= B.msa_backward_scratch_bytes(p) < base + slots * 128 * 64 * 2 + 4096
+    for field, value in (("topk", 33), ("dq_mode", B.DQ_RECOMPUTE), ("dq_mode", B.DQ_ATOMIC_POOL),
+                         ("dq_mode", B.DQ_ATOMIC_POOL_BF16)):
+        with pytest.raises(NotImplementedError):
+            B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, field: value}))
+    with pytest.raises(ValueError):   # 63 blocks of 128 cannot hold 8192 tokens
+        B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "num_kblocks": 63}))
 
 
 def test_missing_library_raises_unavailable(monkeypatch):

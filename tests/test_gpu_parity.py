@@ -100,15 +100,50 @@ def test_small_cases_full_parity(case, num_cus, dq_mode):
     assert torch.all(dv.cpu()[torch.from_numpy(~attended)] == 0)
 
 
+# Key block 128 (the pages' production block size): documents that end
+# inside the first or the second 64-key half of a block, diagonal blocks
+# whose second half lies after the chunk, junk slots, both head dims and
+# both walk regimes.
+SMALL128 = {
+    "tiny_b128": lambda: make_workload("tiny", block=128, topk=3),
+    "ragged_b128_junk": lambda: _inject_junk(make_workload(
+        "tiny", lengths=[200, 0, 77, 512, 9, 300], num_kv_heads=2, head_dim=128, block=128, topk=4,
+        seed=21), 5),
+    "d64_b128": lambda: make_workload("tiny", lengths=[1000, 129], num_kv_heads=2, head_dim=64,
+                                      block=128, topk=5, seed=22),
+    "large_walk_b128": lambda: make_workload("tiny", lengths=[4096], num_kv_heads=2, head_dim=128,
+                                             block=128, topk=8, seed=23),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL128))
+@pytest.mark.parametrize("num_cus", [None, 7])
+def test_small_cases_block128_full_parity(case, num_cus):
+    w = SMALL128[case]()
+    print(f"[case] {case} num_cus={num_cus} T={w.total_tokens} Hkv={w.num_kv_heads} "
+          f"D={w.head_dim} k={w.topk} block={w.block}", flush=True)
+    p = TL.problem_for(w, num_cus, B.DQ_DS_BUFFER)
+    t = TL.to_dev(w)
+    sched = TL.run_schedule(w, p, t)
+    want = TL.compare_schedule(w, p, sched)
+    out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
+    mode = O.backward_dense if w.total_tokens <= 1024 else O.backward_gathered
+    rdq, rdk, rdv, _, rout, rlse = mode(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block,
+                                        w.scale)
+    TL.assert_out_lse(out, lse, rout, rlse)
+    TL.assert_grads(dq, dk, dv, rdq, rdk, rdv)
+
+
 FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
 
 
 @pytest.mark.parametrize("name,dq_mode", [(n, B.DQ_RECOMPUTE) for n in FULL] +
                          [(n, B.DQ_DS_BUFFER) for n in FULL] + [("single8k", B.DQ_ATOMIC_POOL),
-                                                                ("single8k", B.DQ_ATOMIC_POOL_BF16)])
+                                                                ("single8k", B.DQ_ATOMIC_POOL_BF16),
+                                                                ("single8k_b128", B.DQ_DS_BUFFER)])
 def test_full_size_configs_sampled(name, dq_mode):
     print(f"[case] full-size {name} dq_mode={dq_mode}", flush=True)
-    w = make_workload(name)
+    w = make_workload("single8k", block=128) if name == "single8k_b128" else make_workload(name)
     p = TL.problem_for(w, dq_mode=dq_mode)
     t = TL.to_dev(w)
     sched = TL.run_schedule(w, p, t)

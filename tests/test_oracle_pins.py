@@ -108,7 +108,8 @@ def _sdpa_reference(q, k, v, do, layout, scale, mask_fn):
     return out.numpy(), lse.numpy(), dq.numpy(), dk.numpy(), dv.numpy()
 
 
-@pytest.mark.parametrize("lens,block,d", [([64], 16, 16), ([40, 16, 72], 16, 8), ([128], 64, 32)])
+@pytest.mark.parametrize("lens,block,d", [([64], 16, 16), ([40, 16, 72], 16, 8), ([128], 64, 32),
+                                          ([200, 77], 128, 16)])
 def test_all_blocks_selected_is_dense_causal_attention(lens, block, d):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     layout = O.DocLayout(cu, block)

@@ -50,9 +50,18 @@ def _brute_csr(sel, layout):
 
 @pytest.mark.parametrize("seed", range(6))
 def test_csr_matches_brute_force(seed):
+    _csr_brute_force_case(seed, None)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_csr_matches_brute_force_block128(seed):
+    _csr_brute_force_case(100 + seed, 128)
+
+
+def _csr_brute_force_case(seed, block):
     rng = np.random.default_rng(seed)
-    lens = [int(x) for x in rng.integers(0, 120, size=rng.integers(1, 5))]
-    block = int(rng.choice([8, 16, 32, 64]))
+    lens = [int(x) for x in rng.integers(0, 120 if block is None else 500, size=rng.integers(1, 5))]
+    block = int(rng.choice([8, 16, 32, 64])) if block is None else block
     hkv, k = int(rng.integers(1, 4)), int(rng.integers(1, 6))
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     layout = O.DocLayout(cu, block)
