@@ -103,3 +103,17 @@ def test_binding_type_checks():
         B._expect(torch.zeros(2, dtype=torch.int64), "cu_seqlens", torch.int32, (2,))
     with pytest.raises(ValueError):
         B._expect(torch.zeros(3, dtype=torch.int32), "cu_seqlens", torch.int32, (2,))
+
+
+def test_autograd_entry_refuses_host_tensors():
+    """The autograd entry point only marshals: host tensors are refused before
+    anything runs (there is no CPU path)."""
+    import torch
+    from block_sparse_attention_k2q_amd.autograd import msa_attention
+    p = B.Problem.make([0, 64], 1, 64, 1)
+    q = torch.zeros(64, 16, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(64, 1, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    sel = torch.zeros(1, 8, 1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        msa_attention(q, kv, kv, cu, sel, p)
