@@ -30,6 +30,16 @@ MiniMax-M3 MSA kernels):
 * Walk rule and task table (msa_schedule page, ``rows_per_cta``,
   ``chunk_map``, ``grid_launch_bound``, ``ROWS_PER_CTA_*``, and the
   ``scheduler_metadata`` column order).
+* Index scorer and top-k block selection (``index_select``).  The pages name
+  the scorer (msa_bindings page: MSAKernels lists ``fmha_sm100``, the
+  scorer, beside the planner) and its sizes (msa_schedule page, module data:
+  ``INDEX_DIM``, ``NUM_INDEX_HEADS``, ``TOPK_BLOCKS``) but not its scoring
+  function; the reading taken here is the plainest one that produces the
+  selection the attention consumes: per index head, the score of key block
+  b for chunk c is  (sum of the chunk's index queries) . (mean of the
+  block's index keys); the chunk keeps its own (diagonal) block plus the
+  topk - 1 highest-scoring earlier blocks of its document, ties to the
+  smaller block id, fewer when fewer exist; ids ascending, -1 padding.
 
 Floating point is fp64 throughout; bf16 inputs are widened exactly.
 """
@@ -418,3 +428,55 @@ def chunks_selecting_block(sched: dict, i: int, row: int) -> list[tuple[int, int
     d = int(layout.row_doc[row])
     return [(i, int(layout.chunk_off[d]) + int(x) // layout.chunk)
             for x in qi[rp[row]:rp[row + 1]]]
+
+
+# ---------------------------------------------------------------------------
+# Index scorer and top-k block selection (reading stated in the module header)
+# ---------------------------------------------------------------------------
+
+def index_scores(qi, ki, cu_seqlens, block: int):
+    """Per document d: S[d] of shape [H, C_d, nb_d] with S[h, c, b] =
+    (sum of the index queries of chunk c) . (mean of the index keys of block
+    b), over the tokens of the document (a chunk or block cut by the
+    document end uses the tokens it has), and the matching magnitude
+    M[h, c, b] = sum_x |qsum_x| * mean_j |k_jx| (the scale of the score's
+    rounding error in a float32 evaluation)."""
+    layout = DocLayout(cu_seqlens, block)
+    q, k = f64(qi), f64(ki)
+    out = []
+    for d in range(layout.docs):
+        t0, n = int(layout.cu[d]), int(layout.lens[d])
+        nc, nb = int(layout.nchunks[d]), int(layout.nblocks[d])
+        H, X = q.shape[1], q.shape[2]
+        qsum = np.zeros((H, nc, X))
+        qabs = np.zeros((H, nc, X))
+        for c in range(nc):
+            rows = q[t0 + QUERY_CHUNK * c: t0 + min(QUERY_CHUNK * (c + 1), n)]
+            qsum[:, c] = rows.sum(axis=0)
+            qabs[:, c] = np.abs(rows).sum(axis=0)
+        kbar = np.zeros((H, nb, X))
+        kabs = np.zeros((H, nb, X))
+        for b in range(nb):
+            rows = k[t0 + block * b: t0 + min(block * (b + 1), n)]
+            kbar[:, b] = rows.mean(axis=0)
+            kabs[:, b] = np.abs(rows).mean(axis=0)
+        out.append((np.einsum("hcx,hbx->hcb", qsum, kbar), np.einsum("hcx,hbx->hcb", qabs, kabs)))
+    return layout, out
+
+
+def index_select(qi, ki, cu_seqlens, block: int, topk: int) -> np.ndarray:
+    """sel int32 [H, C, topk]: the diagonal block of each chunk plus its
+    topk - 1 best-scoring earlier blocks (ties to the smaller id), ascending,
+    -1 padding."""
+    layout, scores = index_scores(qi, ki, cu_seqlens, block)
+    H = f64(qi).shape[1]
+    sel = np.full((H, layout.C, topk), -1, dtype=np.int32)
+    for d, (S, _) in enumerate(scores):
+        for h in range(H):
+            for c in range(int(layout.nchunks[d])):
+                diag = (QUERY_CHUNK * c) // block
+                cand = np.arange(diag)
+                order = np.lexsort((cand, -S[h, c, :diag]))    # score descending, then id
+                keep = sorted([diag] + [int(b) for b in cand[order[:topk - 1]]])
+                sel[h, int(layout.chunk_off[d]) + c, :len(keep)] = keep
+    return sel
