@@ -27,11 +27,14 @@ MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_
 SCHED_ERR_DROPPED, SCHED_ERR_GEOMETRY = 0, 1
 DQ_RECOMPUTE, DQ_ATOMIC_POOL, DQ_DS_BUFFER, DQ_ATOMIC_POOL_BF16 = 0, 1, 2, 3
 MAX_DOC_CHUNKS = 1 << 18
+INDEX_DIM = 128                  # MSA_INDEX_DIM (msa.h)
+INDEX_MAX_DOC_BLOCKS = 4096      # MSA_INDEX_MAX_DOC_BLOCKS (msa.h)
 
 EXPORTED = (
     "msa_device_check", "msa_schedule_layout_of", "msa_build_schedule", "msa_forward",
     "msa_backward_scratch_bytes", "msa_backward", "msa_backward_preprocess", "msa_backward_main",
     "msa_backward_dq", "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
+    "msa_index_scratch_bytes", "msa_index_select",
 )
 
 
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "msa_backward_postprocess": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
             "msa_grid_launch_bound": ([ctypes.c_int64, ctypes.c_int32], ctypes.c_int64),
             "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "msa_index_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+            "msa_index_select": ([P, vp, vp, i32p, vp, i32p, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -221,6 +226,34 @@ def msa_forward(p: Problem, q, k, v, cu_seqlens, sched, out, lse, stream=None) -
     ps = p.c_struct()
     _check(lib().msa_forward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(sched),
                              _ptr(out), _ptr(lse), _stream(stream)), "msa_forward")
+
+
+def msa_index_scratch_bytes(p: Problem) -> int:
+    ps = p.c_struct()
+    out = ctypes.c_size_t(0)
+    _check(lib().msa_index_scratch_bytes(ctypes.byref(ps), ctypes.byref(out)), "msa_index_scratch_bytes")
+    return int(out.value)
+
+
+def msa_index_select(p: Problem, qi, ki, cu_seqlens, scratch, sel, stream=None) -> None:
+    """Index scorer + top-k block selection into sel int32 [Hkv, C, topk]."""
+    T, hkv = p.total_tokens, p.num_kv_heads
+    _expect(qi, "qi", torch.bfloat16, (T, hkv, INDEX_DIM))
+    _expect(ki, "ki", torch.bfloat16, (T, hkv, INDEX_DIM))
+    _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
+    _expect(scratch, "scratch", torch.uint8, (msa_index_scratch_bytes(p),))
+    _expect(sel, "sel", torch.int32, (hkv, p.num_chunks, p.topk))
+    ps = p.c_struct()
+    _check(lib().msa_index_select(ctypes.byref(ps), _ptr(qi), _ptr(ki), _ptr(cu_seqlens), _ptr(scratch),
+                                  _ptr(sel), _stream(stream)), "msa_index_select")
+
+
+def index_select(p: Problem, qi, ki, cu_seqlens, scratch=None, stream=None) -> torch.Tensor:
+    if scratch is None:
+        scratch = torch.empty(msa_index_scratch_bytes(p), dtype=torch.uint8, device=qi.device)
+    sel = torch.empty(p.num_kv_heads, p.num_chunks, p.topk, dtype=torch.int32, device=qi.device)
+    msa_index_select(p, qi, ki, cu_seqlens, scratch, sel, stream)
+    return sel
 
 
 def msa_backward_scratch_bytes(p: Problem) -> int:

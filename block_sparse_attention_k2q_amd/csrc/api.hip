@@ -170,6 +170,34 @@ int msa_backward(const msa_problem* p, const void* q, const void* k, const void*
   return msa_backward_postprocess(p, scratch, dq, dk, dv, stream);
 }
 
+static int check_index_problem(const msa_problem* p) {
+  const int st = check_problem(p);
+  if (st != MSA_OK) return st;
+  const int64_t max_doc_blocks = ((int64_t)p->max_doc_chunks * 8 + p->block_size - 1) / p->block_size;
+  if (max_doc_blocks > MSA_INDEX_MAX_DOC_BLOCKS) return MSA_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_kv_heads * (p->num_chunks + p->num_kblocks) > INT32_MAX) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+int msa_index_scratch_bytes(const msa_problem* p, size_t* bytes) {
+  const int st = check_index_problem(p);
+  if (st != MSA_OK) return st;
+  if (!bytes) return MSA_ERR_INVALID;
+  *bytes = msa::index_scratch_layout(*p).total;
+  return MSA_OK;
+}
+
+int msa_index_select(const msa_problem* p, const void* qi, const void* ki, const int32_t* cu_seqlens,
+                     void* scratch, int32_t* sel, void* stream) {
+  const int st = check_index_problem(p);
+  if (st != MSA_OK) return st;
+  if (!cu_seqlens || !scratch || (p->num_chunks > 0 && !sel) || (p->total_tokens > 0 && (!qi || !ki)))
+    return MSA_ERR_INVALID;
+  if (!aligned16(qi) || !aligned16(ki) || !aligned16(scratch) || ((uintptr_t)sel & 3u) != 0)
+    return MSA_ERR_ALIGN;
+  return hip_status(msa::launch_index_select(*p, qi, ki, cu_seqlens, scratch, sel, (hipStream_t)stream));
+}
+
 int64_t msa_grid_launch_bound(int64_t capacity, int32_t num_cus) {
   if (capacity < 0 || num_cus < 1) return -1;
   return msa::grid_launch_bound(capacity, num_cus);

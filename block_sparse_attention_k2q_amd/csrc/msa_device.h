@@ -183,6 +183,9 @@ __device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// The wave's LDS writes are done (and not moved past this point) before its
+// later LDS reads; the wave's own LDS accesses execute in order.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also fences global
@@ -432,6 +435,27 @@ __device__ __forceinline__ float swap_halves(float x) {
 }
 
 // Index of the last element <= x in a non-decreasing array a[0..n) (a[0] <= x).
+// Block-wide inclusive scan of one int per thread (blockDim.x == NT, a
+// multiple of 64); s_warp holds NT / 64 ints; *total receives the sum.
+template <int NT>
+__device__ int block_inclusive_scan_n(int x, int* s_warp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_warp[w] = x;
+  __syncthreads();
+  int add = 0, tot = 0;
+  for (int k = 0; k < NT / 64; ++k) {
+    if (k < w) add += s_warp[k];
+    tot += s_warp[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return x + add;
+}
+
 __device__ __forceinline__ int upper_bound_minus1(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi)
   while (hi - lo > 1) {

@@ -78,6 +78,31 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   return s;
 }
 
+// Index scorer (scorer.hip): index dimension and the most earlier blocks a
+// chunk can choose from (one LDS score per candidate per wave).
+constexpr int kIndexDim = MSA_INDEX_DIM;
+constexpr int kMaxIndexCandidates = MSA_INDEX_MAX_DOC_BLOCKS;
+
+// Scratch of the index scorer (bytes, 256-aligned): per-document offsets and
+// an error word (int32), chunk query sums fp32 [H, C, kIndexDim], block key
+// means fp32 [H, R, kIndexDim].
+struct IndexScratch {
+  size_t geo, qsum, kbar, total;
+};
+inline IndexScratch index_scratch_layout(const msa_problem& p) {
+  auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+  IndexScratch s;
+  size_t o = 0;
+  s.geo = o; o = a256(o + 4 * (2 * (size_t)p.num_docs + 2 + 8));
+  s.qsum = o; o = a256(o + 4 * (size_t)p.num_kv_heads * p.num_chunks * kIndexDim);
+  s.kbar = o; o = a256(o + 4 * (size_t)p.num_kv_heads * p.num_kblocks * kIndexDim);
+  s.total = o;
+  return s;
+}
+
+hipError_t launch_index_select(const msa_problem& p, const void* qi, const void* ki, const int32_t* cu,
+                               void* scratch, int32_t* sel, hipStream_t stream);
+
 hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const int32_t* sel,
                                  int32_t* sched, const msa_schedule_layout& L, hipStream_t stream);
 hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, const void* v,

@@ -36,23 +36,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Block-wide inclusive scan of one int per thread (blockDim.x == kThreads).
-__device__ int block_inclusive_scan(int x, int* s_warp, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s_warp[w] = x;
-  __syncthreads();
-  int add = 0, tot = 0;
-  for (int k = 0; k < kThreads / 64; ++k) {
-    if (k < w) add += s_warp[k];
-    tot += s_warp[k];
-  }
-  __syncthreads();
-  *total = tot;
-  return x + add;
+__device__ __forceinline__ int block_inclusive_scan(int x, int* s_warp, int* total) {
+  return block_inclusive_scan_n<kThreads>(x, s_warp, total);
 }
 
 constexpr int kZeroPerBlock = 16 * kThreads;   // counters cleared per extra workgroup

@@ -189,3 +189,18 @@ def make_workload(name: str = "tiny", *, lengths=None, num_kv_heads=None, head_d
                     scale=1.0 / math.sqrt(d), sel=np.ascontiguousarray(sel, dtype=np.int32),
                     q=q, k=kk, v=v, do=do)
 
+
+INDEX_DIM = 128           # msa_schedule page, INDEX_DIM
+
+
+def make_index_inputs(w: Workload, seed: int = 0) -> tuple[torch.Tensor, torch.Tensor]:
+    """Synthetic index projections for the index scorer: qi, ki bf16
+    [T, Hkv, INDEX_DIM], N(0, 1), from a generator of their own
+    (PCG64(10000 + seed)), so the attention inputs of ``w`` are unchanged.
+    With such inputs the selection is close to uniform over earlier blocks,
+    like the workloads' own selections."""
+    rng = np.random.Generator(np.random.PCG64(10000 + seed))
+    t = w.total_tokens
+    qi = _bf16_normals(rng, (t, w.num_kv_heads, INDEX_DIM), 1.0)
+    ki = _bf16_normals(rng, (t, w.num_kv_heads, INDEX_DIM), 1.0)
+    return qi, ki

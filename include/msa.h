@@ -185,6 +185,30 @@ int msa_backward_dq(const msa_problem* p, const void* q, const void* k, const vo
 int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk,
                              void* dv, void* stream);
 
+/* Index scorer and top-k block selection: the step that produces `sel`.
+ * msa_bindings: MSAKernels lists the scorer (fmha_sm100) beside the planner;
+ * msa_schedule, module data: INDEX_DIM 128, NUM_INDEX_HEADS 4 (one index
+ * head per KV head here), TOPK_BLOCKS.  The pages do not define the scoring
+ * function; this library's reading, per index head i and chunk c:
+ *   score(c, b) = (sum of the chunk's index queries) . (mean of the index
+ *                 keys of key block b), over the tokens of c's document;
+ *   sel[i, c] = {diagonal block of c} + the topk - 1 best-scoring earlier
+ *               blocks (ties to the smaller id; fewer when fewer exist),
+ *               ascending, -1 padding.
+ * Sums and the dot product are fp32 (a score differs from the exact one by
+ * a few 1e-6 of sum_x |qsum_x| mean|k_x|, so near-ties may order either way).
+ *   qi, ki  : bf16 [T, Hkv, MSA_INDEX_DIM] index queries / keys (device)
+ *   scratch : msa_index_scratch_bytes bytes (device, 16-byte aligned)
+ *   sel     : int32 [Hkv, C, topk] (device), written in full
+ * Documents may hold at most MSA_INDEX_MAX_DOC_BLOCKS key blocks
+ * (MSA_ERR_UNSUPPORTED otherwise).  cu_seqlens that disagree with the host
+ * sizes leave every row empty (-1). */
+#define MSA_INDEX_DIM 128
+#define MSA_INDEX_MAX_DOC_BLOCKS 4096
+int msa_index_scratch_bytes(const msa_problem* p, size_t* bytes);
+int msa_index_select(const msa_problem* p, const void* qi, const void* ki, const int32_t* cu_seqlens,
+                     void* scratch, int32_t* sel, void* stream);
+
 /* Grid size the main backward kernel is launched with (msa_schedule:
  * grid_launch_bound(capacity, num_cus), capacity = Hkv * C * topk). */
 int64_t msa_grid_launch_bound(int64_t capacity, int32_t num_cus);

@@ -460,7 +460,7 @@ def index_scores(qi, ki, cu_seqlens, block: int):
             rows = k[t0 + block * b: t0 + min(block * (b + 1), n)]
             kbar[:, b] = rows.mean(axis=0)
             kabs[:, b] = np.abs(rows).mean(axis=0)
-        out.append((np.einsum("hcx,hbx->hcb", qsum, kbar), np.einsum("hcx,hbx->hcb", qabs, kabs)))
+        out.append((qsum @ kbar.transpose(0, 2, 1), qabs @ kabs.transpose(0, 2, 1)))
     return layout, out
 
 

@@ -117,3 +117,13 @@ def test_autograd_entry_refuses_host_tensors():
     sel = torch.zeros(1, 8, 1, dtype=torch.int32)
     with pytest.raises(ValueError):
         msa_attention(q, kv, kv, cu, sel, p)
+
+
+def test_index_scorer_limits():
+    p = B.Problem.make([0, 8192], 4, 128, 16)
+    base = 4 * 1024 * 128 * 4 + 4 * 128 * 128 * 4     # chunk query sums + block key means (fp32)
+    assert base <= B.msa_index_scratch_bytes(p) < base + 1024
+    long_doc = B.Problem.make([0, 300000], 1, 128, 16)   # 4688 key blocks in one document
+    with pytest.raises(NotImplementedError):
+        B.msa_index_scratch_bytes(long_doc)
+    assert B.msa_index_scratch_bytes(B.Problem.make([0, 262144], 1, 128, 16)) > 0   # 4096 blocks
