@@ -241,10 +241,17 @@ __device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__
 }
 
 // Direct global -> LDS copy of 16 bytes per lane from a wave-uniform base
-// plus a per-lane 32-bit byte offset: the scalar-base addressing form of the
-// load, so no 64-bit address arithmetic runs per copy.
+// plus a per-lane 32-bit byte offset, issued as a buffer load (the base in a
+// buffer descriptor, the offset in a VGPR), so no 64-bit address arithmetic
+// runs per copy.  The buffer form also keeps the compiler's LDS waits exact:
+// the global form is a flat-encoded instruction, and while one is pending
+// the compiler waits for every outstanding LDS read (lgkmcnt(0)) wherever it
+// needs only the oldest.
 __device__ __forceinline__ void dma16_at(const void* sbase, uint32_t byte_off, void* lds_wave_base) {
-  dma16((const char*)sbase + byte_off, lds_wave_base);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(sbase), (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)byte_off, 0, 0, 0);
 }
 
 // Copies of key blocks (K and V rows of KV head i) into swizzled tile pairs.
