@@ -202,7 +202,6 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     lds_sync();   // block j landed for every wave; all are done with block j-1's buffers
     if (j + 1 < nblk) copy(v_next, v, take_block(rem_v, bsel));
     if (j + 2 < nblk) copy(k_next2, k, take_block(rem_k, bsel));
-    after_lds_copies();   // no LDS read is pending here: lets the reads below be waited for one by one
     consume(kt, vt, take_block(rem_c, bsel));
   };
   for (int j = 0; j < nblk; j += 6) {

@@ -142,21 +142,22 @@ __device__ __forceinline__ bf16x8 lds_tr_operand_swz8b(const bf16* tile, int col
 }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l of the wave writes
-// bytes [16 l, 16 l + 16) after lds_wave_base (wave-uniform).
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
-                                   0);
+// bytes [16 l, 16 l + 16) after lds_wave_base (wave-uniform), reading from a
+// wave-uniform base plus the lane's 32-bit byte offset.
+// runs per copy.  The buffer form also keeps the compiler's LDS waits exact:
+// the global form is a flat-encoded instruction, and while one is pending
+// the compiler waits for every outstanding LDS read (lgkmcnt(0)) wherever it
+// needs only the oldest.
+__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t byte_off, void* lds_wave_base) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(sbase), (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
+                                           (int)byte_off, 0, 0, 0);
 }
 
 // Wait until this wave has no outstanding vector-memory operations.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// The compiler counts a direct global->LDS copy as an LDS-counter event as
-// well; while one is pending it waits for every outstanding LDS read
-// (lgkmcnt(0)) instead of only the one it needs.  Called right after the
-// copies are issued, at a point with no LDS reads outstanding, this wait
-// costs nothing and lets the following LDS reads be waited for one by one.
-__device__ __forceinline__ void after_lds_copies() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
@@ -213,6 +214,15 @@ struct KVTiles {
   bf16 v[kBlock * D];
 };
 
+// Direct global -> LDS copy of 16 bytes per lane from a per-lane 64-bit
+// address, in the global (flat-encoded) form; lane l writes bytes
+// [16 l, 16 l + 16) after lds_wave_base.  Only stage_kv uses it: its kernel
+// has no registers to spare for the buffer form's descriptors and offsets.
+__device__ __forceinline__ void dma16_global(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0,
+                                   0);
+}
+
 // Copy key block b (K and V rows of KV head i) into a swizzled tile pair with
 // 64-bit addresses computed per copy (for kernels with no registers to hold
 // precomputed offsets).  Keys past the document end read the document's last
@@ -235,24 +245,11 @@ __device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__
     const int row = piece * RPP + lrow;
     const int lc = pcol ^ chunk_swizzle<CPR>(row);
     const int64_t off = (int64_t)(b * kBlock + min(row, kmax)) * row_stride + 8 * lc;
-    dma16(kbase + off, t.k + piece * 512);
-    dma16(vbase + off, t.v + piece * 512);
+    dma16_global(kbase + off, t.k + piece * 512);
+    dma16_global(vbase + off, t.v + piece * 512);
   }
 }
 
-// Direct global -> LDS copy of 16 bytes per lane from a wave-uniform base
-// plus a per-lane 32-bit byte offset, issued as a buffer load (the base in a
-// buffer descriptor, the offset in a VGPR), so no 64-bit address arithmetic
-// runs per copy.  The buffer form also keeps the compiler's LDS waits exact:
-// the global form is a flat-encoded instruction, and while one is pending
-// the compiler waits for every outstanding LDS read (lgkmcnt(0)) wherever it
-// needs only the oldest.
-__device__ __forceinline__ void dma16_at(const void* sbase, uint32_t byte_off, void* lds_wave_base) {
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(sbase), (short)0, 0x7FFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_wave_base, 16,
-                                           (int)byte_off, 0, 0, 0);
-}
 
 // Copies of key blocks (K and V rows of KV head i) into swizzled tile pairs.
 // Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
