@@ -176,9 +176,6 @@ __device__ __forceinline__ void store_bf16x8_stream(bf16* p, bf16x8 v) {
 __device__ __forceinline__ bf16x8 load_bf16x8_stream(const bf16* p) {
   return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
-__device__ __forceinline__ void store_bf16x4_stream(bf16* p, bf16x4 v) {
-  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
-}
 __device__ __forceinline__ void store_bf16x4(bf16* p, bf16x4 v) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v);
 }
@@ -251,58 +248,9 @@ __device__ __forceinline__ void stage_kv(KVTiles<D>& t, const bf16* __restrict__
 }
 
 
-// Copies of key blocks (K and V rows of KV head i) into swizzled tile pairs.
-// Wave w copies pieces w, w + NWAVES, ... (a piece = 64 chunks of 16 bytes =
-// 64 / CPR rows); lane l supplies physical chunk l of its piece.  The lane's
-// byte offsets relative to a block's first key are computed once; keys past
-// the document end (last block of a document only) read the document's last
-// key instead: they are masked out of the softmax, and their values are finite.
-template <int D, int NWAVES>
-struct KvCopier {
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int RPP = 64 / CPR;            // rows per piece
-  static constexpr int N = kBlock / RPP / NWAVES;  // pieces per wave and tensor
-  uint32_t off[N];
-  int hkv, row_stride, w, lane;
-
-  __device__ __forceinline__ KvCopier(int Hkv, int w_, int lane_)
-      : hkv(Hkv), row_stride(Hkv * D), w(w_), lane(lane_) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) off[n] = byte_offset(n, row_of(n));
-  }
-  __device__ __forceinline__ int row_of(int n) const { return (n * NWAVES + w) * RPP + lane / CPR; }
-  __device__ __forceinline__ uint32_t byte_offset(int n, int r) const {
-    const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row_of(n));
-    return (uint32_t)(r * row_stride + 8 * lc) * 2u;
-  }
-  __device__ __forceinline__ void operator()(KVTiles<D>& t, const bf16* __restrict__ k,
-                                             const bf16* __restrict__ v, int tok0, int len, int b,
-                                             int i) const {
-    const int64_t first = ((int64_t)(tok0 + b * kBlock) * hkv + i) * D;
-    const bf16* kb = k + first;
-    const bf16* vb = v + first;
-    const int kmax = len - 1 - b * kBlock;       // last valid key offset in this block
-    if (kmax >= kBlock - 1) {
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const int piece = n * NWAVES + w;
-        dma16_at(kb, off[n], t.k + piece * 512);
-        dma16_at(vb, off[n], t.v + piece * 512);
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const int piece = n * NWAVES + w;
-        const uint32_t o = byte_offset(n, min(row_of(n), kmax));
-        dma16_at(kb, o, t.k + piece * 512);
-        dma16_at(vb, o, t.v + piece * 512);
-      }
-    }
-  }
-};
-
 // Copy key block b of one tensor (K, say) of KV head i into a swizzled
-// kBlock x D tile; same piece layout and end-of-document rule as KvCopier.
+// kBlock x D tile; 64 / CPR rows per wave-sized piece, keys past the document
+// end read the document's last key (masked by the consumer).
 template <int D, int NWAVES>
 __device__ __forceinline__ void stage_block(bf16* tile, const bf16* __restrict__ src, int tok0, int len,
                                             int b, int Hkv, int i, int w, int lane) {
@@ -366,60 +314,6 @@ __device__ __forceinline__ int compact_tiles(const int32_t* __restrict__ row, in
   }
   return __popcll(mask);
 }
-
-// Register-staged copy of key block b (K and V rows of KV head i) into
-// swizzled kBlock x D tiles (same piece layout and end-of-document rule as
-// stage_block): load_k() / load_v() issue plain 16-byte global loads into
-// registers, store_k() / store_v() write them to LDS once they have arrived.  Unlike
-// direct global->LDS copies, the loads leave the LDS alone until the wave
-// writes.  Addresses are a wave-uniform base plus this lane's 32-bit byte
-// offsets, computed once (K and V share them).
-template <int D, int NWAVES>
-struct KvStager {
-  static constexpr int CPR = D / 8;
-  static constexpr int RPP = 64 / CPR;
-  static constexpr int N = kBlock / RPP / NWAVES;
-  bf16x8 rk[N], rv[N];
-  uint32_t off[N];
-  int hkv, w, lane;
-
-  __device__ __forceinline__ KvStager(int Hkv, int w_, int lane_) : hkv(Hkv), w(w_), lane(lane_) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) off[n] = byte_offset(n, row_of(n));
-  }
-  __device__ __forceinline__ int row_of(int n) const { return (n * NWAVES + w) * RPP + lane / CPR; }
-  __device__ __forceinline__ uint32_t byte_offset(int n, int r) const {
-    const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row_of(n));
-    return (uint32_t)(r * hkv * D + 8 * lc) * 2u;
-  }
-  // Load one tensor's rows of block b into dst (K or V: same layout).
-  __device__ __forceinline__ void load(bf16x8 (&dst)[N], const bf16* __restrict__ src, int tok0, int len,
-                                       int b, int i) const {
-    const char* base = (const char*)(src + ((int64_t)(tok0 + b * kBlock) * hkv + i) * D);
-    const int kmax = len - 1 - b * kBlock;
-    if (kmax >= kBlock - 1) {
-#pragma unroll
-      for (int n = 0; n < N; ++n) dst[n] = load_bf16x8((const bf16*)(base + off[n]));
-    } else {
-#pragma unroll
-      for (int n = 0; n < N; ++n) dst[n] = load_bf16x8((const bf16*)(base + byte_offset(n, min(row_of(n), kmax))));
-    }
-  }
-  __device__ __forceinline__ void load_k(const bf16* __restrict__ k, int tok0, int len, int b, int i) {
-    load(rk, k, tok0, len, b, i);
-  }
-  __device__ __forceinline__ void load_v(const bf16* __restrict__ v, int tok0, int len, int b, int i) {
-    load(rv, v, tok0, len, b, i);
-  }
-  __device__ __forceinline__ void store_k(bf16* tile) const {
-#pragma unroll
-    for (int n = 0; n < N; ++n) *reinterpret_cast<bf16x8*>(tile + (n * NWAVES + w) * 512 + lane * 8) = rk[n];
-  }
-  __device__ __forceinline__ void store_v(bf16* tile) const {
-#pragma unroll
-    for (int n = 0; n < N; ++n) *reinterpret_cast<bf16x8*>(tile + (n * NWAVES + w) * 512 + lane * 8) = rv[n];
-  }
-};
 
 // acc + sum of the 8 bf16 values of v (dot products with (1, 1) on bf16 pairs).
 __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
