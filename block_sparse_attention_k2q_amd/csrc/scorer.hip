@@ -94,8 +94,20 @@ __global__ __launch_bounds__(kIdxThreads) void index_pool_kernel(
   const int count = min(span, len - first);
   const bf16* src = (is_key ? ki : qi) + ((int64_t)(tok0 + first) * H + i) * kIndexDim + 2 * lane;
   float a0 = 0.f, a1 = 0.f;
-  for (int t = 0; t < count; ++t) {
-    const bf16x2 x = *reinterpret_cast<const bf16x2*>(src + (int64_t)t * H * kIndexDim);
+  const int64_t stride = (int64_t)H * kIndexDim;
+  int t = 0;
+  for (; t + 4 <= count; t += 4) {   // four loads in flight, then added in token order
+    bf16x2 x[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) x[m] = *reinterpret_cast<const bf16x2*>(src + (t + m) * stride);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      a0 += (float)x[m][0];
+      a1 += (float)x[m][1];
+    }
+  }
+  for (; t < count; ++t) {
+    const bf16x2 x = *reinterpret_cast<const bf16x2*>(src + t * stride);
     a0 += (float)x[0];
     a1 += (float)x[1];
   }
@@ -140,26 +152,39 @@ __global__ __launch_bounds__(kIdxThreads) void index_select_kernel(
   const float4* qv = reinterpret_cast<const float4*>(qsum + unit * kIndexDim + 8 * sl);
   const float4 q0 = qv[0], q1 = qv[1];
   const float* krows = kbar + ((int64_t)i * R + doc_blk_off[d]) * kIndexDim + 8 * sl;
-  for (int b0 = 0; b0 < n; b0 += 4) {
-    const int b = b0 + grp;
-    float part = 0.f;
-    if (b < n) {
-      const float4* kv = reinterpret_cast<const float4*>(krows + (int64_t)b * kIndexDim);
-      const float4 k0 = kv[0], k1 = kv[1];
-      part = q0.x * k0.x;
-      part = fmaf(q0.y, k0.y, part);
-      part = fmaf(q0.z, k0.z, part);
-      part = fmaf(q0.w, k0.w, part);
-      part = fmaf(q1.x, k1.x, part);
-      part = fmaf(q1.y, k1.y, part);
-      part = fmaf(q1.z, k1.z, part);
-      part = fmaf(q1.w, k1.w, part);
+  // Four blocks per group per round, their loads issued together.
+  constexpr int kRound = 4;
+  for (int b0 = 0; b0 < n; b0 += 4 * kRound) {
+    float4 k0[kRound], k1[kRound];
+#pragma unroll
+    for (int t = 0; t < kRound; ++t) {
+      const int b = b0 + 4 * t + grp;
+      if (b < n) {
+        const float4* kv = reinterpret_cast<const float4*>(krows + (int64_t)b * kIndexDim);
+        k0[t] = kv[0];
+        k1[t] = kv[1];
+      } else {
+        k0[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+        k1[t] = k0[t];
+      }
     }
-    part += __shfl_xor(part, 8, 64);
-    part += __shfl_xor(part, 4, 64);
-    part += __shfl_xor(part, 2, 64);
-    part += __shfl_xor(part, 1, 64);
-    if (b < n && sl == 0) sc[b] = part;
+#pragma unroll
+    for (int t = 0; t < kRound; ++t) {
+      const int b = b0 + 4 * t + grp;
+      float part = q0.x * k0[t].x;
+      part = fmaf(q0.y, k0[t].y, part);
+      part = fmaf(q0.z, k0[t].z, part);
+      part = fmaf(q0.w, k0[t].w, part);
+      part = fmaf(q1.x, k1[t].x, part);
+      part = fmaf(q1.y, k1[t].y, part);
+      part = fmaf(q1.z, k1[t].z, part);
+      part = fmaf(q1.w, k1[t].w, part);
+      part += __shfl_xor(part, 8, 64);
+      part += __shfl_xor(part, 4, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 1, 64);
+      if (b < n && sl == 0) sc[b] = part;
+    }
   }
   wave_lds_sync();   // the wave's score writes before its reads
 
