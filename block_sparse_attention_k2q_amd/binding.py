@@ -184,6 +184,15 @@ def _stream(stream) -> Optional[int]:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _on_device(*tensors):
+    """The tensors' one GPU, made current for the call (the library launches on
+    the current device, on that device's current stream unless one is given)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(str(d) for d in devs)}")
+    return torch.cuda.device(next(iter(devs)))
+
+
 def _expect(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -210,9 +219,10 @@ def msa_build_schedule(p: Problem, cu_seqlens: torch.Tensor, sel: torch.Tensor, 
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
     _expect(sel, "sel", torch.int32, (p.num_kv_heads, p.num_chunks, p.topk))
     _expect(sched, "sched", torch.int32, (L.total,))
-    ps = p.c_struct()
-    _check(lib().msa_build_schedule(ctypes.byref(ps), _ptr(cu_seqlens), _ptr(sel), _ptr(sched),
-                                    _stream(stream)), "msa_build_schedule")
+    with _on_device(cu_seqlens, sel, sched):
+        ps = p.c_struct()
+        _check(lib().msa_build_schedule(ctypes.byref(ps), _ptr(cu_seqlens), _ptr(sel), _ptr(sched),
+                                        _stream(stream)), "msa_build_schedule")
 
 
 def msa_forward(p: Problem, q, k, v, cu_seqlens, sched, out, lse, stream=None) -> None:
@@ -223,9 +233,10 @@ def msa_forward(p: Problem, q, k, v, cu_seqlens, sched, out, lse, stream=None) -
     _expect(lse, "lse", torch.float32, (T, hq))
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
     _expect(sched, "sched", torch.int32, (msa_schedule_layout_of(p).total,))
-    ps = p.c_struct()
-    _check(lib().msa_forward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(sched),
-                             _ptr(out), _ptr(lse), _stream(stream)), "msa_forward")
+    with _on_device(q, k, v, cu_seqlens, sched, out, lse):
+        ps = p.c_struct()
+        _check(lib().msa_forward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(sched),
+                                 _ptr(out), _ptr(lse), _stream(stream)), "msa_forward")
 
 
 def msa_index_scratch_bytes(p: Problem) -> int:
@@ -243,9 +254,10 @@ def msa_index_select(p: Problem, qi, ki, cu_seqlens, scratch, sel, stream=None) 
     _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
     _expect(scratch, "scratch", torch.uint8, (msa_index_scratch_bytes(p),))
     _expect(sel, "sel", torch.int32, (hkv, p.num_chunks, p.topk))
-    ps = p.c_struct()
-    _check(lib().msa_index_select(ctypes.byref(ps), _ptr(qi), _ptr(ki), _ptr(cu_seqlens), _ptr(scratch),
-                                  _ptr(sel), _stream(stream)), "msa_index_select")
+    with _on_device(qi, ki, cu_seqlens, scratch, sel):
+        ps = p.c_struct()
+        _check(lib().msa_index_select(ctypes.byref(ps), _ptr(qi), _ptr(ki), _ptr(cu_seqlens), _ptr(scratch),
+                                      _ptr(sel), _stream(stream)), "msa_index_select")
 
 
 def index_select(p: Problem, qi, ki, cu_seqlens, scratch=None, stream=None) -> torch.Tensor:
@@ -286,35 +298,39 @@ def msa_backward(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched, scratch
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
     _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
     _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
-    ps = p.c_struct()
-    _check(lib().msa_backward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                              _ptr(lse), _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq),
-                              _ptr(dk), _ptr(dv), _stream(stream)), "msa_backward")
+    with _on_device(q, k, v, out, dout, lse, cu_seqlens, sched, scratch, dq, dk, dv):
+        ps = p.c_struct()
+        _check(lib().msa_backward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                  _ptr(lse), _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _stream(stream)), "msa_backward")
 
 
 def msa_backward_preprocess(p: Problem, out, dout, scratch, stream=None) -> None:
     _check_bwd_inputs(p, None, None, None, out, dout, None, None, None, scratch)
-    ps = p.c_struct()
-    _check(lib().msa_backward_preprocess(ctypes.byref(ps), _ptr(out), _ptr(dout), _ptr(scratch),
-                                         _stream(stream)), "msa_backward_preprocess")
+    with _on_device(out, dout, scratch):
+        ps = p.c_struct()
+        _check(lib().msa_backward_preprocess(ctypes.byref(ps), _ptr(out), _ptr(dout), _ptr(scratch),
+                                             _stream(stream)), "msa_backward_preprocess")
 
 
 def msa_backward_main(p: Problem, q, k, v, dout, lse, cu_seqlens, sched, scratch, stream=None) -> None:
     _check_bwd_inputs(p, q, k, v, None, dout, lse, cu_seqlens, sched, scratch)
-    ps = p.c_struct()
-    _check(lib().msa_backward_main(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
-                                   _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _stream(stream)),
-           "msa_backward_main")
+    with _on_device(q, k, v, dout, lse, cu_seqlens, sched, scratch):
+        ps = p.c_struct()
+        _check(lib().msa_backward_main(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                       _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _stream(stream)),
+               "msa_backward_main")
 
 
 def msa_backward_dq(p: Problem, q, k, v, dout, lse, cu_seqlens, sched, scratch, dq, stream=None) -> None:
     _check_bwd_inputs(p, q, k, v, None, dout, lse, cu_seqlens, sched, scratch)
     T, hq, D = p.total_tokens, p.num_q_heads, p.head_dim
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
-    ps = p.c_struct()
-    _check(lib().msa_backward_dq(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
-                                 _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq), _stream(stream)),
-           "msa_backward_dq")
+    with _on_device(q, k, v, dout, lse, cu_seqlens, sched, scratch, dq):
+        ps = p.c_struct()
+        _check(lib().msa_backward_dq(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                     _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq), _stream(stream)),
+               "msa_backward_dq")
 
 
 def msa_backward_postprocess(p: Problem, scratch, dq, dk, dv, stream=None) -> None:
@@ -323,9 +339,10 @@ def msa_backward_postprocess(p: Problem, scratch, dq, dk, dv, stream=None) -> No
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
     _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
     _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
-    ps = p.c_struct()
-    _check(lib().msa_backward_postprocess(ctypes.byref(ps), _ptr(scratch), _ptr(dq), _ptr(dk), _ptr(dv),
-                                          _stream(stream)), "msa_backward_postprocess")
+    with _on_device(scratch, dq, dk, dv):
+        ps = p.c_struct()
+        _check(lib().msa_backward_postprocess(ctypes.byref(ps), _ptr(scratch), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              _stream(stream)), "msa_backward_postprocess")
 
 
 def msa_grid_launch_bound(capacity: int, num_cus: int) -> int:

@@ -127,3 +127,9 @@ def test_index_scorer_limits():
     with pytest.raises(NotImplementedError):
         B.msa_index_scratch_bytes(long_doc)
     assert B.msa_index_scratch_bytes(B.Problem.make([0, 262144], 1, 128, 16)) > 0   # 4096 blocks
+
+
+def test_tensors_on_different_devices_are_refused():
+    import torch
+    with pytest.raises(ValueError):
+        B._on_device(torch.zeros(1), torch.zeros(1, device="meta"))
