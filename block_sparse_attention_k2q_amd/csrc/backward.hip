@@ -459,9 +459,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
 //    32*(w >> 1) .. +31 of the block: K and V of those keys live in
 //    registers as the A operands of S^T = K Q^T and dP^T = V dO^T (loaded
 //    once per bucket segment), each lane owning one query column;
-//  * the Q and dO rows of the half (and its LSE / Delta) arrive in LDS by
-//    direct global->LDS loads into one of two swizzled buffers, the next
-//    task's copy in flight while the current one is consumed;
+//  * the Q and dO rows of the half arrive in LDS by direct global->LDS
+//    loads into one of two swizzled buffers, the next task's copy in flight
+//    while the current one is consumed (each lane's LSE and Delta are loaded
+//    into registers one task ahead);
 //  * P^T goes to an LDS tile for dV += P^T dO, then dS^T (kept in
 //    registers meanwhile) overwrites it for dK += dS^T Q; each wave owns
 //    2 (head dim 128) or 1 (head dim 64) of the 32 x 32 output tiles of dV

@@ -1,4 +1,7 @@
-// Query-parallel dQ kernel of the MSA backward on gfx950 (MSA_DQ_RECOMPUTE).
+// Query-parallel dQ kernels of the MSA backward on gfx950: dq_kernel
+// (MSA_DQ_RECOMPUTE) below, and dq_from_ds_kernel (MSA_DQ_DS_BUFFER, the
+// default) further down.  Both walk a chunk's kept 64-key tiles (a selected
+// block of 128 keys is two tiles).
 //
 // dQ_p = scale * sum_j dS_pj k_j with dS = P (dP - Delta), P = exp(s - LSE)
 // (msa_backward_sm100 page: the dQ^T contraction; kernels page: Delta from
@@ -183,8 +186,8 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
 }
 
 // dQ from stored dS (MSA_DQ_DS_BUFFER): one workgroup per (chunk, index
-// head), 4 waves x 32 query rows.  The chunk's kept blocks stream through a
-// three-stage ring: while block n is consumed, blocks n+1 and n+2 are in
+// head), 4 waves x 32 query rows.  The chunk's kept 64-key tiles ("blocks"
+// below) stream through a three-stage ring: while block n is consumed, blocks n+1 and n+2 are in
 // flight (K by direct loads into one of three swizzled LDS buffers, the
 // wave's dS^T operands, stored by the main kernel in MFMA operand order so
 // that each 16-key step is one contiguous 1 KiB load per wave, into
