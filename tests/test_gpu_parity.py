@@ -140,10 +140,15 @@ FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
 @pytest.mark.parametrize("name,dq_mode", [(n, B.DQ_RECOMPUTE) for n in FULL] +
                          [(n, B.DQ_DS_BUFFER) for n in FULL] + [("single8k", B.DQ_ATOMIC_POOL),
                                                                 ("single8k", B.DQ_ATOMIC_POOL_BF16),
-                                                                ("single8k_b128", B.DQ_DS_BUFFER)])
+                                                                ("single8k_b128", B.DQ_DS_BUFFER),
+                                                                ("varlen8_b128", B.DQ_DS_BUFFER),
+                                                                ("long64k_b128", B.DQ_DS_BUFFER)])
 def test_full_size_configs_sampled(name, dq_mode):
     print(f"[case] full-size {name} dq_mode={dq_mode}", flush=True)
-    w = make_workload("single8k", block=128) if name == "single8k_b128" else make_workload(name)
+    if name.endswith("_b128"):   # the same workload at key block 128
+        w = make_workload(name[:-len("_b128")], block=128)
+    else:
+        w = make_workload(name)
     p = TL.problem_for(w, dq_mode=dq_mode)
     t = TL.to_dev(w)
     sched = TL.run_schedule(w, p, t)
