@@ -116,23 +116,23 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     // S^T = K Q^T: two 32-key tiles; operands of k step s+1 are read while
     // step s runs.
     floatx16 st[2] = {floatx16{}, floatx16{}};
-    // K operands two k steps ahead: one step (two MFMAs) does not cover the
-    // LDS latency.
-    bf16x8 ak[3][2];
+    // K operands three k steps ahead: fewer do not cover the LDS latency
+    // (measured: two steps ahead is 2.5 % slower).
+    bf16x8 ak[4][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 3; ++s) {
       ak[s][0] = lds_row8<CPR>(kt, n32, 16 * s + 8 * h);
       ak[s][1] = lds_row8<CPR>(kt, 32 + n32, 16 * s + 8 * h);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if (s + 2 < KS) {
-        ak[(s + 2) % 3][0] = lds_row8<CPR>(kt, n32, 16 * (s + 2) + 8 * h);
-        ak[(s + 2) % 3][1] = lds_row8<CPR>(kt, 32 + n32, 16 * (s + 2) + 8 * h);
+      if (s + 3 < KS) {
+        ak[(s + 3) % 4][0] = lds_row8<CPR>(kt, n32, 16 * (s + 3) + 8 * h);
+        ak[(s + 3) % 4][1] = lds_row8<CPR>(kt, 32 + n32, 16 * (s + 3) + 8 * h);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) st[a] = mfma32(ak[s % 3][a], qf[s], st[a]);
+      for (int a = 0; a < 2; ++a) st[a] = mfma32(ak[s % 4][a], qf[s], st[a]);
       __builtin_amdgcn_sched_barrier(0);
     }
 
