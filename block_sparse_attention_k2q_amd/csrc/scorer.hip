@@ -127,8 +127,10 @@ __device__ __forceinline__ bool better(float s, int b, float s2, int b2) {
 __global__ __launch_bounds__(kIdxThreads) void index_select_kernel(
     const float* __restrict__ qsum, const float* __restrict__ kbar, const int32_t* __restrict__ doc_chunk_off,
     const int32_t* __restrict__ doc_blk_off, const int32_t* __restrict__ err, int H, int C, int R, int B,
-    int K, int num_docs, int32_t* __restrict__ sel) {
-  __shared__ float s_score[kIdxWaves][kMaxIndexCandidates];
+    int K, int num_docs, int cand_cap, int32_t* __restrict__ sel) {
+  // cand_cap floats of scores per wave (the longest document's block count,
+  // at most kMaxIndexCandidates), sized at launch
+  extern __shared__ float s_score[];
   const int w = wave_id(), lane = lane_id();
   const int64_t unit = (int64_t)blockIdx.x * kIdxWaves + w;   // = i * C + g
   if (unit >= (int64_t)H * C) return;   // whole waves; the kernel has no workgroup barrier
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(kIdxThreads) void index_select_kernel(
   const int c = g - doc_chunk_off[d];
   const int diag = (kChunk * c) / B;   // candidates: blocks 0 .. diag - 1
   const int n = diag;
-  float* sc = s_score[w];
+  float* sc = s_score + w * cand_cap;
 
   // Scores: lane group grp = lane / 16 takes block b0 + grp; lane sl = lane % 16
   // of the group multiplies dimensions 8 sl .. 8 sl + 7 in order, then the
@@ -252,10 +254,13 @@ hipError_t launch_index_select(const msa_problem& p, const void* qi, const void*
                        dim3(kIdxThreads), 0, stream, (const bf16*)qi, (const bf16*)ki, cu, doc_chunk_off,
                        doc_blk_off, err, H, C, R, B, p.num_docs, qsum, kbar);
   const int64_t sel_units = (int64_t)H * C;
+  // candidates of a chunk: the earlier blocks of its document
+  const int64_t max_doc_blocks = ((int64_t)p.max_doc_chunks * kChunk + B - 1) / B;
+  const int cand_cap = (int)((max_doc_blocks + 63) / 64 * 64);
   if (sel_units > 0)
     hipLaunchKernelGGL(index_select_kernel, dim3((unsigned)((sel_units + kIdxWaves - 1) / kIdxWaves)),
-                       dim3(kIdxThreads), 0, stream, qsum, kbar, doc_chunk_off, doc_blk_off, err, H, C, R, B,
-                       p.topk, p.num_docs, sel);
+                       dim3(kIdxThreads), (size_t)kIdxWaves * cand_cap * sizeof(float), stream, qsum, kbar,
+                       doc_chunk_off, doc_blk_off, err, H, C, R, B, p.topk, p.num_docs, cand_cap, sel);
   return hipGetLastError();
 }
 
