@@ -847,7 +847,12 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
   // Two workgroups per walk, one per query half of every task tile.
   auto go_kv = [&](auto kern) {
     const int sub = p.block_size / kBlock;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * sub * grid)), dim3(kBwdThreads), 0, stream, (const bf16*)q,
+    // Units u = 2 walk + half; with two tiles per block, tile t of unit u is
+    // workgroup ((u >> 3) << 4) | (t << 3) | (u & 7), so the launch rounds the
+    // units up to whole groups of eight (units past the walks return at once).
+    const int64_t units = 2 * grid;
+    const int64_t nwg = sub == 1 ? units : (units + 7) / 8 * 16;
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),

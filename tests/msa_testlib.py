@@ -96,3 +96,26 @@ def assert_grads(dq, dk, dv, ref_dq, ref_dk, ref_dv) -> None:
     assert_grad("dq", dq, ref_dq)
     assert_grad("dk", dk, ref_dk)
     assert_grad("dv", dv, ref_dv)
+
+
+def inject_junk(w, seed):
+    """Replace some slots by repeats, out-of-range, non-causal and negative ids."""
+    rng = np.random.default_rng(seed)
+    sel = w.sel.copy()
+    H, C, K = sel.shape
+    layout = O.DocLayout(w.cu_seqlens, w.block)
+    for _ in range(max(4, C // 8)):
+        i, g = int(rng.integers(H)), int(rng.integers(C))
+        d, c = layout.chunk_local(g)
+        s = int(rng.integers(K))
+        kind = int(rng.integers(4))
+        if kind == 0:
+            sel[i, g, s] = sel[i, g, 0]                          # repeat
+        elif kind == 1:
+            sel[i, g, s] = int(layout.nblocks[d]) + int(rng.integers(3))   # past the document
+        elif kind == 2:
+            sel[i, g, s] = min(int(layout.nblocks[d]) - 1, (8 * c) // w.block + 1)  # maybe non-causal
+        else:
+            sel[i, g, s] = -2 - int(rng.integers(5))              # negative, not the empty marker
+    w.sel = sel
+    return w

@@ -20,32 +20,9 @@ import msa_testlib as TL
 pytestmark = pytest.mark.gpu
 
 
-def _inject_junk(w, seed):
-    """Replace some slots by repeats, out-of-range, non-causal and negative ids."""
-    rng = np.random.default_rng(seed)
-    sel = w.sel.copy()
-    H, C, K = sel.shape
-    layout = O.DocLayout(w.cu_seqlens, w.block)
-    for _ in range(max(4, C // 8)):
-        i, g = int(rng.integers(H)), int(rng.integers(C))
-        d, c = layout.chunk_local(g)
-        s = int(rng.integers(K))
-        kind = int(rng.integers(4))
-        if kind == 0:
-            sel[i, g, s] = sel[i, g, 0]                          # repeat
-        elif kind == 1:
-            sel[i, g, s] = int(layout.nblocks[d]) + int(rng.integers(3))   # past the document
-        elif kind == 2:
-            sel[i, g, s] = min(int(layout.nblocks[d]) - 1, (8 * c) // w.block + 1)  # maybe non-causal
-        else:
-            sel[i, g, s] = -2 - int(rng.integers(5))              # negative, not the empty marker
-    w.sel = sel
-    return w
-
-
 SMALL = {
     "tiny": lambda: make_workload("tiny"),
-    "ragged_docs_junk": lambda: _inject_junk(make_workload(
+    "ragged_docs_junk": lambda: TL.inject_junk(make_workload(
         "tiny", lengths=[200, 0, 77, 512, 9], num_kv_heads=2, head_dim=128, topk=5, seed=11), 3),
     "d64_two_heads": lambda: make_workload("tiny", lengths=[300, 129], num_kv_heads=2, head_dim=64,
                                            topk=3, seed=12),
@@ -106,7 +83,7 @@ def test_small_cases_full_parity(case, num_cus, dq_mode):
 # both walk regimes.
 SMALL128 = {
     "tiny_b128": lambda: make_workload("tiny", block=128, topk=3),
-    "ragged_b128_junk": lambda: _inject_junk(make_workload(
+    "ragged_b128_junk": lambda: TL.inject_junk(make_workload(
         "tiny", lengths=[200, 0, 77, 512, 9, 300], num_kv_heads=2, head_dim=128, block=128, topk=4,
         seed=21), 5),
     "d64_b128": lambda: make_workload("tiny", lengths=[1000, 129], num_kv_heads=2, head_dim=64,
@@ -117,7 +94,7 @@ SMALL128 = {
 
 
 @pytest.mark.parametrize("case", list(SMALL128))
-@pytest.mark.parametrize("num_cus", [None, 7])
+@pytest.mark.parametrize("num_cus", [None, 7, 1])   # 1: the grid has no spare walk
 def test_small_cases_block128_full_parity(case, num_cus):
     w = SMALL128[case]()
     print(f"[case] {case} num_cus={num_cus} T={w.total_tokens} Hkv={w.num_kv_heads} "
