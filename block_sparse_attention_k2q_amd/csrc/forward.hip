@@ -40,6 +40,17 @@ __device__ __forceinline__ int take_block(uint64_t& rem, int bsel) {
   return __builtin_amdgcn_readlane(bsel, slot);
 }
 
+// Maximum and sum over the lane pair (l, l ^ 32): one lane swap between the
+// wave's halves, no LDS round trip.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[a][j]);
-    mx = fmaxf(mx, swap_halves(mx)) * c2;   // max in the scaled log2 domain
+    mx = max_halves(mx) * c2;   // max in the scaled log2 domain
     // Lazy rescale: the running max m only moves when a score exceeds it by
     // more than kRescaleLog2, so P = exp2(s - m) stays <= 2^kRescaleLog2 and
     // the O accumulators are rescaled only on the (rare) blocks that move it.
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     if (j + 5 < nblk) step(j + 5, kb2, vb1, vb0, kb1);
   }
 
-  const float l_tot = l + swap_halves(l);
+  const float l_tot = sum_halves(l);
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   bf16* orow = out + qrow * D;

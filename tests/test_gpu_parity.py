@@ -47,6 +47,26 @@ def _empty_rows_workload():
 SMALL["empty_chunks"] = _empty_rows_workload
 
 
+def _scaled_late_keys(factor):
+    """Keys of the blocks from 4 on scaled by `factor` (exact in bf16: a
+    power of two), so chunks whose first selected block is an early one meet
+    scores far above its max later: the forward's running max must move and
+    rescale what it has summed (by about 2^35 at factor 8; at factor 64 an
+    unrescaled sum would overflow fp32), and the backward runs with LSE up
+    to about 330."""
+    def make():
+        w = make_workload("tiny", lengths=[1024], num_kv_heads=1, head_dim=128, topk=6, seed=31)
+        k = w.k.float().clone()
+        k[4 * w.block:] *= factor
+        w.k = k.to(torch.bfloat16)
+        return w
+    return make
+
+
+SMALL["growing_max"] = _scaled_late_keys(8.0)
+SMALL["overflowing_max"] = _scaled_late_keys(64.0)
+
+
 @pytest.mark.parametrize("case", list(SMALL))
 @pytest.mark.parametrize("num_cus,dq_mode", [(None, B.DQ_RECOMPUTE), (7, B.DQ_RECOMPUTE),
                                              (None, B.DQ_ATOMIC_POOL), (7, B.DQ_ATOMIC_POOL),
