@@ -132,7 +132,7 @@ def main() -> int:
             return 2
         WORKLOAD = "single8k_b128"
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU "
               "path: the method shards by KV head with no exchange, see the design notes.",
               file=sys.stderr)
         return 2
