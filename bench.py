@@ -60,7 +60,7 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def traffic_profile_path(kernel_name: str) -> str:
-    """profiles/<kernel>_single8k_hbm_traffic.md for a kernel name such as
+    """profiles/<kernel>_<workload>_hbm_traffic.md for a kernel name such as
     'dq_kernel<128>' (non-alphanumerics become underscores)."""
     stem = re.sub(r"[^A-Za-z0-9]+", "_", kernel_name).strip("_")
     return os.path.join(ROOT, "profiles", f"{stem}_{WORKLOAD}_hbm_traffic.md")
@@ -121,16 +121,20 @@ def main() -> int:
     ap.add_argument("--block", type=int, choices=(64, 128), default=64,
                     help="key block size: 64 (the headline workload) or 128 (the same workload at the "
                          "pages' production block size; dq mode ds only)")
+    ap.add_argument("--workload", choices=("single8k", "varlen8", "long64k", "zipf16k"), default="single8k",
+                    help="single8k is the headline workload; the others are the remaining full-size "
+                         "configurations (packed varlen, 64k context at top-32, Zipf-skewed selection)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run a plain device-to-device copy of this many MiB "
                          "three times (the known-size reference for HBM byte counters)")
     args = ap.parse_args()
     global WORKLOAD
+    WORKLOAD = args.workload
     if args.block == 128:
         if args.dq_mode != "ds":
             print("key block 128 runs with --dq-mode ds only", file=sys.stderr)
             return 2
-        WORKLOAD = "single8k_b128"
+        WORKLOAD = args.workload + "_b128"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU "
               "path: the method shards by KV head with no exchange, see the design notes.",
@@ -144,7 +148,7 @@ def main() -> int:
 
     dev = torch.device("cuda", 0)
     num_cus = B.msa_device_check(0)
-    w = make_workload("single8k", block=args.block)
+    w = make_workload(args.workload, block=args.block)
     dq_mode = {"recompute": B.DQ_RECOMPUTE, "ds": B.DQ_DS_BUFFER, "atomic": B.DQ_ATOMIC_POOL,
                "atomic_bf16": B.DQ_ATOMIC_POOL_BF16}[args.dq_mode]
     p = B.Problem.make(w.cu_seqlens, w.num_kv_heads, w.head_dim, w.topk, num_cus=num_cus,
@@ -256,8 +260,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO, diagonal + uniform block selection)",
-        "config": {"workload": "single8k: 1 document T=8192, 4 KV heads x 16 query heads, D=128, "
-                               f"key block {args.block}, chunk 8, top-k 16",
+        "config": {"workload": f"{args.workload}: {len(w.cu_seqlens) - 1} document(s), T={w.total_tokens}, "
+                               f"{w.num_kv_heads} KV heads x 16 query heads, D={w.head_dim}, "
+                               f"key block {args.block}, chunk 8, top-k {w.topk}",
                    "selected_pairs": n_pairs, "num_cus": num_cus, "dq_mode": args.dq_mode},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(x, 4) for n, x in per_kernel.items()},
