@@ -13,11 +13,12 @@ Workload: one 8192-token document, 4 KV heads x 16 query heads, head dim
 Prints one JSON line.  ``value`` is useful TFLOP/s of forward + backward:
 every selected (index head, chunk, block) pair counts as one 128 x 64 tile,
 2 contractions forward and 5 backward, each 2*128*64*128 FLOPs; recomputed
-contractions are not counted.  After the warmup, K steps with a HIP event
-between every two kernels give the per-kernel breakdown; then the timed K
-steps carry events only around the kernel with the largest time, whose
-mean launch duration (HIP events on torch's current stream, the stream the
-kernels are launched on) gives the ``roofline`` object.
+contractions are not counted.  The warmup steps carry a HIP event between
+every two kernels, which picks the kernel with the largest time; the timed
+K steps that follow carry events only around that kernel, whose mean launch
+duration (HIP events on torch's current stream, the stream the kernels are
+launched on) gives the ``roofline`` object; K more steps with events
+between all kernels then give the per-kernel breakdown.
 """
 from __future__ import annotations
 
@@ -182,30 +183,23 @@ def main() -> int:
         B.msa_backward_postprocess(p, scratch, dq, dk, dv)
         mark(6)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    n_pairs = int(B.schedule_views(p, sched)["desc"][0].item())
-
     def event_rows(n):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n)]
 
-    # Per-kernel breakdown: K steps with an event between every two kernels.
-    events = event_rows(args.steps)
-    for s in range(args.steps):
-        step(events[s])
+    # Warmup, with an event between every two kernels: the kernel with the
+    # largest time gets the events of the timed steps.
+    wev = event_rows(args.warmup)
+    for s in range(args.warmup):
+        step(wev[s])
     torch.cuda.synchronize()
-    per_kernel = {n: float(np.mean([events[s][j].elapsed_time(events[s][j + 1])
-                                    for s in range(args.steps)])) for j, n in enumerate(names)}
-    per_kernel_median = {n: float(np.median([events[s][j].elapsed_time(events[s][j + 1])
-                                             for s in range(args.steps)])) for j, n in enumerate(names)}
     timed = {"forward": 1, "bwd_main": 3, "bwd_dq": 4}
-    dominant = max(timed, key=lambda kname: per_kernel[kname])
+    dominant = "bwd_main" if not wev else max(
+        timed, key=lambda kname: np.mean([e[timed[kname]].elapsed_time(e[timed[kname] + 1]) for e in wev]))
     jd = timed[dominant]
 
-    # Timed region: K steps, events only around the dominant kernel (the
-    # roofline's launch duration), so the whole-step clock carries as little
-    # instrumentation as possible.
+    # Timed region: K steps, right after the warmup, with events only around
+    # the dominant kernel (the roofline's launch duration), so the step
+    # clock carries as little instrumentation as possible.
     tev = event_rows(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -215,6 +209,18 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     dominant_ms = float(np.mean([tev[s][jd].elapsed_time(tev[s][jd + 1]) for s in range(args.steps)]))
+
+    n_pairs = int(B.schedule_views(p, sched)["desc"][0].item())
+
+    # Per-kernel breakdown: K more steps with an event between every two kernels.
+    events = event_rows(args.steps)
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    per_kernel = {n: float(np.mean([events[s][j].elapsed_time(events[s][j + 1])
+                                    for s in range(args.steps)])) for j, n in enumerate(names)}
+    per_kernel_median = {n: float(np.median([events[s][j].elapsed_time(events[s][j + 1])
+                                             for s in range(args.steps)])) for j, n in enumerate(names)}
 
     # One cold step after a 512 MiB write has pushed the inputs out of the caches.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -241,6 +247,21 @@ def main() -> int:
     # useful contractions per pair done by each kernel
     pool = dq_mode in (B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16)
     useful = {"forward": fwd_f, "bwd_main": (5 if pool else 4) * gemm, "bwd_dq": (0 if pool else 1) * gemm}
+    # Compulsory HBM bytes of each kernel (every tensor it must read or write
+    # once), for the HBM-bound steps' GB/s against the 8 TB/s peak.
+    T, hq, hkv, D = w.total_tokens, 16 * w.num_kv_heads, w.num_kv_heads, w.head_dim
+    qb, kb = T * hq * D * 2, T * hkv * D * 2               # one bf16 [T, Hq, D] / [T, Hkv, D] tensor
+    pool_bytes = {B.DQ_ATOMIC_POOL: 2 * qb, B.DQ_ATOMIC_POOL_BF16: qb}.get(dq_mode, 0)
+    ds_bytes = n_pairs * 128 * w.block * 2 if dq_mode == B.DQ_DS_BUFFER else 0
+    compulsory = {
+        "forward": qb + 2 * kb + qb + T * hq * 4,
+        "bwd_pre": 2 * qb + T * hq * 4 + 4 * kb + pool_bytes,
+        "bwd_main": 2 * qb + 2 * kb + 2 * T * hq * 4 + 4 * kb + ds_bytes,
+        "bwd_dq": ds_bytes + kb + qb if dq_mode == B.DQ_DS_BUFFER else (
+            0 if pool else 2 * qb + 2 * kb + 2 * T * hq * 4 + qb),
+        "bwd_post": 4 * kb + 2 * kb + (pool_bytes + qb if pool else 0),
+    }
+    gbps = {n: b / (per_kernel[n] * 1e-3) / 1e9 for n, b in compulsory.items() if b > 0 and per_kernel[n] > 0}
     tflops = {kname: n_pairs * f / (per_kernel[kname] * 1e-3) / 1e12 for kname, f in useful.items()
               if per_kernel[kname] > 0 and f > 0}
     bwd_ms = per_kernel["bwd_pre"] + per_kernel["bwd_main"] + per_kernel["bwd_dq"] + per_kernel["bwd_post"]
@@ -275,6 +296,8 @@ def main() -> int:
                           "value": round(value * unmasked_fraction, 3), "unit": "TFLOP/s"},
         "kernels_useful_tflops": {n: round(x, 2) for n, x in tflops.items()},
         "kernels_pct_peak": {n: round(100.0 * x / PEAK_BF16_TFLOPS, 2) for n, x in tflops.items()},
+        "kernels_compulsory_GBps": {n: round(x, 1) for n, x in gbps.items()},
+        "kernels_pct_hbm_peak": {n: round(100.0 * x / PEAK_HBM_GBS, 1) for n, x in gbps.items()},
         "forward_pct_peak": round(100.0 * tflops["forward"] / PEAK_BF16_TFLOPS, 2),
         "backward_useful_tflops": round(bwd_tflops, 2),
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
