@@ -327,12 +327,6 @@ __device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
   return acc;
 }
 
-// Value held by lane (l ^ 32).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
-}
-
-// Index of the last element <= x in a non-decreasing array a[0..n) (a[0] <= x).
 // Block-wide inclusive scan of one int per thread (blockDim.x == NT, a
 // multiple of 64); s_warp holds NT / 64 ints; *total receives the sum.
 template <int NT>
@@ -354,6 +348,7 @@ __device__ int block_inclusive_scan_n(int x, int* s_warp, int* total) {
   return x + add;
 }
 
+// Index of the last element <= x in a non-decreasing array a[0..n) (a[0] <= x).
 __device__ __forceinline__ int upper_bound_minus1(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi)
   while (hi - lo > 1) {
