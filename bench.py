@@ -192,9 +192,12 @@ def main() -> int:
     for s in range(args.warmup):
         step(wev[s])
     torch.cuda.synchronize()
+    # The choice uses the last warmup step: the first launch of each kernel
+    # also loads its code, so with a single warmup step the main backward
+    # kernel (4 of the 7 contractions per pair) is taken.
     timed = {"forward": 1, "bwd_main": 3, "bwd_dq": 4}
-    dominant = "bwd_main" if not wev else max(
-        timed, key=lambda kname: np.mean([e[timed[kname]].elapsed_time(e[timed[kname] + 1]) for e in wev]))
+    dominant = "bwd_main" if len(wev) < 2 else max(
+        timed, key=lambda kname: wev[-1][timed[kname]].elapsed_time(wev[-1][timed[kname] + 1]))
     jd = timed[dominant]
 
     # Timed region: K steps, right after the warmup, with events only around

@@ -1,0 +1,39 @@
+"""bench.py end to end: on the GPU one short run prints one JSON line with
+the fields the measurement needs (throughput, roofline of the dominant
+kernel with its launch duration, per-kernel times and HBM rates); asked for
+more than one GPU it refuses before touching any."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.gpu
+def test_bench_json_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "kernels_ms",
+                "kernels_compulsory_GBps"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0
+    roof = d["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    assert roof["launch_ms"] > 0 and roof["kernel"].startswith("backward_kv_kernel")
+    assert d["config"]["selected_pairs"] == 61696
+
+
+def test_bench_refuses_several_gpus():
+    # exits before touching a GPU, so it runs on the CPU too
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60, cwd=ROOT)
+    assert r.returncode == 2 and "one GPU" in r.stderr
