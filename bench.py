@@ -53,10 +53,15 @@ def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of what the kernel is built from: its source file, the shared
+    device header and the compiler flags that file gets."""
+    from block_sparse_attention_k2q_amd import build as msa_build
     h = hashlib.sha256()
     for rel in (KERNEL_FILES[kernel], "msa_device.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_k2q_amd", "csrc", rel), "rb") as f:
             h.update(f.read())
+    flags = msa_build.FLAGS + msa_build.PER_SOURCE_FLAGS.get(KERNEL_FILES[kernel], [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

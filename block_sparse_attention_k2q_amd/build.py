@@ -1,17 +1,24 @@
 """Build libmsa.so (gfx950 only) in-tree with hipcc.
 
 ``python -m block_sparse_attention_k2q_amd.build`` compiles every HIP source
-under csrc/ into one shared library next to this file.  Flags:
+under csrc/ to an object (in parallel) and links them into one shared
+library next to this file.  Flags:
   --offload-arch=gfx950        CDNA4 only, no other targets
   -munsafe-fp-atomics          fp32 atomicAdd lowers to the hardware atomic
   -packed-fp32-ops disabled    packed fp32 VALU forms are kept out of the code
+Per source (PER_SOURCE_FLAGS): the backward and dQ kernels are scheduled
+with the compiler's max-ILP strategy, measured 0.6 % (KV backward) and 3 %
+(dQ) faster than the default; the forward is faster with the default.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -19,28 +26,50 @@ LIB = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-munsafe-fp-atomics",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+PER_SOURCE_FLAGS = {
+    "backward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "dq.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always, even when one is present) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *sources()]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(line for line in (res.stderr or "").splitlines()
-                     if "packed-fp32-ops" not in line)
     if res.returncode != 0:
+        errs = "\n".join(line for line in (res.stderr or "").splitlines()
+                         if "packed-fp32-ops" not in line)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always, even when one is present) and return its path."""
+    tmp = LIB + ".tmp"
+    objdir = tempfile.mkdtemp(prefix="msa_build_")
+    try:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            extra = PER_SOURCE_FLAGS.get(os.path.basename(src), [])
+            jobs.append(([HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj],
+                         obj))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+                f.result()
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[obj for _, obj in jobs]],
+             verbose)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     os.replace(tmp, LIB)
     return LIB
 
