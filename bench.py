@@ -37,6 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6          # MI355X dense bf16 MFMA: 256 CUs x 4096 FLOP
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "single8k"
 KERNEL_FILES = {"forward": "forward.hip", "bwd_main": "backward.hip", "bwd_dq": "dq.hip"}
+KERNEL_FILES_RECOMPUTE = dict(KERNEL_FILES, bwd_dq="dq_recompute.hip")
 KERNEL_NAMES = {  # per dq mode
     "recompute": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, false>",
                   "bwd_dq": "dq_kernel<128>"},
@@ -52,15 +53,16 @@ def pair_flops(block: int, head_dim: int) -> tuple[int, int]:
     return 2 * tile, 5 * tile
 
 
-def kernel_source_hash(kernel: str) -> str:
+def kernel_source_hash(kernel: str, mode: str = "ds") -> str:
     """Hash of what the kernel is built from: its source file, the shared
     device header and the compiler flags that file gets."""
     from block_sparse_attention_k2q_amd import build as msa_build
     h = hashlib.sha256()
-    for rel in (KERNEL_FILES[kernel], "msa_device.h"):
+    files = KERNEL_FILES_RECOMPUTE if mode == "recompute" else KERNEL_FILES
+    for rel in (files[kernel], "msa_device.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_k2q_amd", "csrc", rel), "rb") as f:
             h.update(f.read())
-    flags = msa_build.FLAGS + msa_build.PER_SOURCE_FLAGS.get(KERNEL_FILES[kernel], [])
+    flags = msa_build.FLAGS + msa_build.PER_SOURCE_FLAGS.get(files[kernel], [])
     h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
@@ -82,7 +84,7 @@ def measured_traffic(kernel: str, mode: str):
         return None
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not src or not val or src.group(1) != kernel_source_hash(kernel):
+    if not src or not val or src.group(1) != kernel_source_hash(kernel, mode):
         return None
     return float(val.group(1))
 

@@ -118,6 +118,10 @@ hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k
                               const void* dout, const float* lse, const int32_t* cu,
                               const int32_t* sched, const msa_schedule_layout& L, const void* scratch,
                               void* dq, hipStream_t stream);
+hipError_t launch_dq_recompute(const msa_problem& p, const void* q, const void* k, const void* v,
+                               const void* dout, const float* lse, const int32_t* cu, const int32_t* sched,
+                               const msa_schedule_layout& L, const void* scratch, void* dq,
+                               hipStream_t stream);
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
                                        void* dv, hipStream_t stream);
 
