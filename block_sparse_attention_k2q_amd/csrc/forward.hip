@@ -22,7 +22,16 @@
 //    and a lazy rescale (O is rescaled only when the running max grows by
 //    more than 2^8), and O^T += V^T P^T with P^T taken straight from the S^T
 //    accumulators and V^T read by the LDS transpose load;
-//  * out = O / l in bf16, lse = ln(sum exp(scale * s)) in fp32.
+//  * out = O / l in bf16, lse = ln(sum exp(scale * s)) in fp32;
+//  * P enters the O^T products as bf16.  Its rounding moves each weight by up
+//    to 2^-9 relative, which shifts a row by up to about 2^-9 sum_j w_j
+//    |v_j - O| before the final bf16 rounding; that matters only for rows
+//    whose weight sits on a few keys, which are the rows with large |O|.  A
+//    workgroup any of whose rows ends with max |O| >= 1 therefore runs its
+//    tile once more in a plain loop that splits P into bf16 high and low
+//    parts and multiplies both (fp32-accurate weights), and writes that
+//    result instead (measured on the uniform 8K workload: about 1 % of the
+//    tiles, mostly the first chunks of a document).
 #include "msa_device.h"
 #include "msa_internal.h"
 
@@ -31,6 +40,7 @@ namespace msa {
 namespace {
 
 constexpr float kRescaleLog2 = 8.f;
+constexpr float kPreciseAbove = 1.f;  // max |O| of a row from which its tile is redone
 constexpr int kFwdThreads = 256;      // 4 waves, one 32-query MFMA column each
 
 // The next kept block of a selection row: `rem` holds the not yet taken
@@ -229,9 +239,89 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     if (j + 5 < nblk) step(j + 5, kb2, vb1, vb0, kb1);
   }
 
-  const float l_tot = sum_halves(l);
+  float l_tot = sum_halves(l);
+  float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  bool precise;
+  {
+    float amax = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[tt][r]));
+    const bool mine = __builtin_amdgcn_ballot_w64(qvalid && amax * inv >= kPreciseAbove) != 0;
+    // One flag word per wave in a ring buffer no wave reads any more.
+    int* flags = reinterpret_cast<int*>(kb2);
+    lds_sync();
+    if (lane == 0) flags[w] = mine;
+    lds_sync();
+    precise = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
+  }
+  if (precise) {
+    // The tile once more, one block at a time, with P = hi + lo.
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] = floatx16{};
+    m = -INFINITY;
+    l = 0.f;
+    uint64_t rem = kept;
+    for (int j = 0; j < nblk; ++j) {
+      const int b = take_block(rem, bsel);
+      lds_sync();   // every wave is done with the previous block's buffers
+      copy(kb0, k, b);
+      copy(vb0, v, b);
+      wait_vmem();
+      lds_sync();
+      floatx16 st[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) st[a] = mfma32(lds_row8<CPR>(kb0, 32 * a + n32, 16 * s + 8 * h), qf[s], st[a]);
+      if ((b + 1) * kBlock - 1 > p0) {
+        const int klim = min(pq, len - 1) - b * kBlock - 4 * h;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj)
+            st[a][jj] = 32 * a + 8 * (jj >> 2) + (jj & 3) <= klim ? st[a][jj] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, st[a][jj]);
+      mx = max_halves(mx) * c2;
+      if (mx > m) {
+        const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);
+        l *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) o[tt] *= alpha;
+        m = mx;
+      }
+      const float msub = (m == -INFINITY) ? 0.f : m;
+      // k step u of O^T takes registers 8(u%2) .. 8(u%2)+7 of S^T tile u/2
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(fmaf(st[u >> 1][8 * (u & 1) + e], c2, -msub));
+          ph[e] = (bf16)pv;
+          pl[e] = (bf16)(pv - (float)ph[e]);
+        }
+        l = sum_bf16x8(ph, sum_bf16x8(pl, l));
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const bf16x8 av = lds_tr_operand_swz<CPR>(vb0, 32 * tt, lane, 16 * u, 16 * u + 4, 16 * u + 8,
+                                                    16 * u + 12);
+          o[tt] = mfma32(av, ph, o[tt]);
+          o[tt] = mfma32(av, pl, o[tt]);
+        }
+      }
+    }
+    l_tot = sum_halves(l);
+    inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  }
+
   if (!qvalid) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   bf16* orow = out + qrow * D;
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {

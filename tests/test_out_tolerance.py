@@ -1,6 +1,6 @@
 """The per-element bar on the bf16 output (msa_testlib.out_tolerance): it is
 attainable by a correctly rounded bf16 output at every magnitude, it is the
-plain 1e-2 absolute bar below |out| = 2, and it rejects a result two bf16
+plain 1e-2 absolute bar below |out| = 4, and it rejects a result two bf16
 units away from the exact value (CPU)."""
 import numpy as np
 import torch
@@ -28,10 +28,24 @@ def test_round_to_nearest_always_passes():
     assert np.all(np.abs(_bf16(x) - x) <= TL.out_tolerance(x))
 
 
-def test_plain_bar_below_two_and_one_unit_above():
-    x = np.linspace(-1.999, 1.999, 4001)
+def test_plain_bar_below_four_and_one_unit_above():
+    x = np.linspace(-3.999, 3.999, 8001)
     assert np.all(TL.out_tolerance(x) == 1e-2)
-    assert float(TL.out_tolerance(3.0)) == 2.0**-6 and float(TL.out_tolerance(5.0)) == 2.0**-5
+    assert float(TL.out_tolerance(5.0)) == 2.0**-5 and float(TL.out_tolerance(-4.0)) == 2.0**-5
+    assert float(TL.out_tolerance(8.5)) == 2.0**-4
+
+
+def test_plain_bar_on_two_to_four_rejects_one_unit():
+    # on [2, 4) one bf16 unit (2^-6) exceeds the 1e-2 bar: a result one unit
+    # away from a representable exact value fails there
+    ref = np.array([[3.0, 0.0]])
+    off = ref + np.array([[2.0**-6, 0.0]])
+    lse = np.zeros((1, 2))
+    try:
+        TL.assert_out_lse(torch.from_numpy(off), torch.from_numpy(lse), ref, lse)
+    except AssertionError:
+        return
+    raise AssertionError("an error of 2^-6 at |out| = 3 passed")
 
 
 def test_two_units_off_fails():
