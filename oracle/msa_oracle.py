@@ -41,6 +41,13 @@ MiniMax-M3 MSA kernels):
   topk - 1 highest-scoring earlier blocks of its document, ties to the
   smaller block id, fewer when fewer exist; ids ascending, -1 padding.
 
+Evaluation modes of the attention: literal dense (T x T masks per document
+and head), gathered (each chunk over its selected keys only; masked terms are
+exactly 0, so the result is the same), and the batched gathered functions
+(``chunk_rows``, ``backward_batched``, ``key_block_grads``), which evaluate
+the same per-chunk formulas several chunks per library call so that the
+full-size workloads' hot key blocks can be checked in seconds.
+
 Floating point is fp64 throughout; bf16 inputs are widened exactly.
 """
 from __future__ import annotations
@@ -418,6 +425,149 @@ def backward_gathered(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: flo
         lse[np.ix_(tq, heads)] = L
         delta[np.ix_(tq, heads)] = Dl
     return dq, dk, dv, delta, out, lse
+
+
+def _chunk_batches(q, k, v, do, layout: DocLayout, sel_clean, chunks, batch: int):
+    """Group the listed (index head, chunk) pairs by (index head, number of
+    queries, number of selected keys) and yield, per group of at most
+    ``batch`` chunks, fp64 torch tensors of their rows stacked along a batch
+    axis: (members, i, Q [nb, nq*16, D], dO, K [nb, nk, D], V, ktok [nb, nk],
+    vis [nb, nq*16, nk]); members are (position in ``chunks``, token indices
+    of the queries).  vis is the causal visibility (key position <= query
+    position) of each chunk's selected keys; row r = query r // 16, head
+    r % 16 of the index head's group."""
+    import torch
+    G = Q_HEADS_PER_INDEX
+    Dh = q.shape[2]
+    qt, kt, vt, dot = (torch.as_tensor(x) for x in (q, k, v, do))
+    groups: dict = {}
+    for n, (i, g) in enumerate(chunks):
+        d, qpos, keys = chunk_keys(layout, sel_clean, i, g)
+        groups.setdefault((i, len(qpos), len(keys)), []).append((n, int(layout.cu[d]), qpos, keys))
+    for (i, nq, nk), members in groups.items():
+        for s0 in range(0, len(members), batch):
+            part = members[s0:s0 + batch]
+            nb = len(part)
+            qtok = torch.as_tensor(np.stack([t0 + qp for _, t0, qp, _ in part]))
+            ktok = torch.as_tensor(np.stack([t0 + ks for _, t0, _, ks in part]).reshape(nb, nk))
+            Q = qt[qtok.reshape(-1), G * i:G * (i + 1)].double().reshape(nb, nq * G, Dh)
+            dO = dot[qtok.reshape(-1), G * i:G * (i + 1)].double().reshape(nb, nq * G, Dh)
+            K = kt[ktok.reshape(-1), i].double().reshape(nb, nk, Dh)
+            V = vt[ktok.reshape(-1), i].double().reshape(nb, nk, Dh)
+            qpos = torch.as_tensor(np.stack([qp for _, _, qp, _ in part]))
+            kpos = torch.as_tensor(np.stack([ks for _, _, _, ks in part]).reshape(nb, nk))
+            vis = (kpos[:, None, :] <= qpos[:, :, None])
+            vis = vis[:, :, None, :].expand(nb, nq, G, nk).reshape(nb, nq * G, nk)
+            yield [(n, t0 + qp) for n, t0, qp, _ in part], i, Q, dO, K, V, ktok, vis
+
+
+def _softmax_rows(Q, K, V, vis, scale):
+    """Per stacked chunk: s = scale Q K^T over the visible keys, LSE (-inf for
+    a row that sees no key), P = exp(s - LSE) (0 off the visible set), O = P V."""
+    import torch
+    neg = torch.tensor(-np.inf, dtype=torch.float64)
+    zero = torch.zeros((), dtype=torch.float64)
+    any_row = vis.any(dim=2, keepdim=True)
+    S = torch.where(vis, scale * torch.bmm(Q, K.transpose(1, 2)), neg)
+    lse = torch.where(any_row, torch.logsumexp(S, dim=2, keepdim=True), neg)
+    P = torch.where(vis, torch.exp(S - torch.where(any_row, lse, zero)), zero)
+    return lse, P, torch.bmm(P, V)
+
+
+def chunk_rows(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: float, chunks, batch: int = 32):
+    """O, LSE and dQ of the rows of the listed (index head, chunk) pairs, by
+    the same formulas as ``backward_gathered`` (each chunk over all of its
+    selected keys): LSE = ln sum exp(s), P = exp(s - LSE), O = P V,
+    D = rowsum(dO * O), dS = P (dO V^T - D), dQ = scale dS K; chunks are
+    evaluated several at a time (``_chunk_batches``), only their rows read.
+
+    Returns a list of (token indices [nq], head indices [16], O [nq, 16, D],
+    LSE [nq, 16], dQ [nq, 16, D]) in the order of ``chunks``; a row with no
+    visible key gets O = dQ = 0 and LSE = -inf."""
+    import torch
+    layout = DocLayout(cu_seqlens, block)
+    G = Q_HEADS_PER_INDEX
+    result = [None] * len(chunks)
+    for members, i, Q, dO, K, V, _, vis in _chunk_batches(q, k, v, do, layout, sel_clean, chunks, batch):
+        lse, P, O = _softmax_rows(Q, K, V, vis, scale)
+        Dl = (dO * O).sum(dim=2, keepdim=True)
+        dQ = scale * torch.bmm(P * (torch.bmm(dO, V.transpose(1, 2)) - Dl), K)
+        heads = np.arange(G * i, G * (i + 1))
+        for x, (n, tq) in enumerate(members):
+            nq = len(tq)
+            result[n] = (tq, heads, O[x].reshape(nq, G, -1).numpy(), lse[x, :, 0].reshape(nq, G).numpy(),
+                         dQ[x].reshape(nq, G, -1).numpy())
+    return result
+
+
+def backward_batched(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: float, batch: int = 32):
+    """(dq, dk, dv, out, lse) of the whole problem by the formulas of
+    ``chunk_rows``, with every chunk's dK_j = scale sum dS_pj q_p and
+    dV_j = sum P_pj dO_p added into the rows of its keys."""
+    import torch
+    layout = DocLayout(cu_seqlens, block)
+    T, Hq, Dh = q.shape
+    Hkv = k.shape[1]
+    G = Q_HEADS_PER_INDEX
+    dq = np.zeros((T, Hq, Dh))
+    out = np.zeros((T, Hq, Dh))
+    lse = np.full((T, Hq), -np.inf)
+    dk = torch.zeros(T, Hkv, Dh, dtype=torch.float64)
+    dv = torch.zeros(T, Hkv, Dh, dtype=torch.float64)
+    chunks = [(i, g) for i in range(Hkv) for g in range(layout.C)]
+    for members, i, Q, dO, K, V, ktok, vis in _chunk_batches(q, k, v, do, layout, sel_clean, chunks, batch):
+        lse_b, P, O = _softmax_rows(Q, K, V, vis, scale)
+        Dl = (dO * O).sum(dim=2, keepdim=True)
+        dS = P * (torch.bmm(dO, V.transpose(1, 2)) - Dl)
+        dQ = scale * torch.bmm(dS, K)
+        dk[:, i].index_add_(0, ktok.reshape(-1), (scale * torch.bmm(dS.transpose(1, 2), Q)).reshape(-1, Dh))
+        dv[:, i].index_add_(0, ktok.reshape(-1), torch.bmm(P.transpose(1, 2), dO).reshape(-1, Dh))
+        heads = np.arange(G * i, G * (i + 1))
+        for x, (n, tq) in enumerate(members):
+            nq = len(tq)
+            out[np.ix_(tq, heads)] = O[x].reshape(nq, G, -1).numpy()
+            dq[np.ix_(tq, heads)] = dQ[x].reshape(nq, G, -1).numpy()
+            lse[np.ix_(tq, heads)] = lse_b[x, :, 0].reshape(nq, G).numpy()
+    return dq, dk.numpy(), dv.numpy(), out, lse
+
+
+def key_block_grads(q, k, v, do, cu_seqlens, sel_clean, block: int, scale: float, i: int, row: int,
+                    batch: int = 32):
+    """dK and dV of the keys of one k2q CSR row (key block ``row`` of index
+    head ``i``), complete: the sum over every chunk that selects the block.
+
+    Each selecting chunk is evaluated over all of its selected keys, as in
+    ``backward_gathered``: LSE, P and O = P V from the chunk's scores, the
+    preprocess D = rowsum(dO * O); the block's own columns then give
+    dV_j = sum_{p,h} P_pj dO_p and dK_j = scale sum_{p,h} dS_pj q_p with
+    dS_pj = P_pj (dO_p . v_j - D_p).  Chunks are evaluated several at a time
+    (``_chunk_batches``) and only their rows are read, so a row that
+    thousands of chunks select stays within time and memory.
+
+    Returns (token indices of the block's keys, dk [n, D], dv [n, D])."""
+    import torch
+    layout = DocLayout(cu_seqlens, block)
+    d = int(layout.row_doc[row])
+    b = row - int(layout.blk_off[d])
+    t0, n = int(layout.cu[d]), int(layout.lens[d])
+    bkeys = np.arange(b * layout.block, min((b + 1) * layout.block, n))
+    Dh = q.shape[2]
+    dk = torch.zeros(len(bkeys), Dh, dtype=torch.float64)
+    dv = torch.zeros(len(bkeys), Dh, dtype=torch.float64)
+    g0 = int(layout.chunk_off[d])
+    chunks = [(i, g0 + c) for c in range(int(layout.nchunks[d])) if np.any(sel_clean[i, g0 + c] == b)]
+    for _, _, Q, dO, K, V, ktok, vis in _chunk_batches(q, k, v, do, layout, sel_clean, chunks, batch):
+        nb = Q.shape[0]
+        _, P, O = _softmax_rows(Q, K, V, vis, scale)
+        Dl = (dO * O).sum(dim=2, keepdim=True)
+        # the block's keys inside each chunk's key list
+        cols = torch.searchsorted(ktok, torch.as_tensor(t0 + bkeys)[None, :].expand(nb, -1).contiguous())
+        Pb = torch.gather(P, 2, cols[:, None, :].expand(nb, P.shape[1], len(bkeys)))
+        Vb = torch.gather(V, 1, cols[:, :, None].expand(nb, len(bkeys), Dh))
+        dSb = Pb * (torch.bmm(dO, Vb.transpose(1, 2)) - Dl)
+        dv += torch.bmm(Pb.transpose(1, 2), dO).sum(dim=0)
+        dk += scale * torch.bmm(dSb.transpose(1, 2), Q).sum(dim=0)
+    return t0 + bkeys, dk.numpy(), dv.numpy()
 
 
 def chunks_selecting_block(sched: dict, i: int, row: int) -> list[tuple[int, int]]:

@@ -65,6 +65,22 @@ def _scaled_late_keys(factor):
 
 SMALL["growing_max"] = _scaled_late_keys(8.0)
 SMALL["overflowing_max"] = _scaled_late_keys(64.0)
+# Hot buckets checked element by element: block 0 forced for every chunk
+# (1024 tasks in one CSR row, 16 walks of 64), and Zipf-skewed selection.
+SMALL["hot_row_first"] = lambda: make_workload("tiny", lengths=[8192], num_kv_heads=1, head_dim=128, topk=8,
+                                               selection="uniform_first", seed=17)
+SMALL["hot_rows_zipf"] = lambda: make_workload("tiny", lengths=[8192], num_kv_heads=1, head_dim=128, topk=8,
+                                               selection="zipf", seed=18)
+
+
+def _oracle_full(w, sel_clean):
+    """(dq, dk, dv, out, lse) of the whole problem: literal dense masks up to
+    1024 tokens, the batched gathered evaluation above."""
+    if w.total_tokens <= 1024:
+        dq, dk, dv, _, out, lse = O.backward_dense(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block,
+                                                   w.scale)
+        return dq, dk, dv, out, lse
+    return O.backward_batched(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale)
 
 
 @pytest.mark.parametrize("case", list(SMALL))
@@ -82,8 +98,7 @@ def test_small_cases_full_parity(case, num_cus, dq_mode):
     want = TL.compare_schedule(w, p, sched)
     out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
     sel_clean = want["sel_clean"]
-    mode = O.backward_dense if w.total_tokens <= 1024 else O.backward_gathered
-    rdq, rdk, rdv, _, rout, rlse = mode(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale)
+    rdq, rdk, rdv, rout, rlse = _oracle_full(w, sel_clean)
     TL.assert_out_lse(out, lse, rout, rlse)
     TL.assert_grads(dq, dk, dv, rdq, rdk, rdv)
     # keys no query attends get exactly zero gradient
@@ -124,14 +139,33 @@ def test_small_cases_block128_full_parity(case, num_cus):
     sched = TL.run_schedule(w, p, t)
     want = TL.compare_schedule(w, p, sched)
     out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
-    mode = O.backward_dense if w.total_tokens <= 1024 else O.backward_gathered
-    rdq, rdk, rdv, _, rout, rlse = mode(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block,
-                                        w.scale)
+    rdq, rdk, rdv, rout, rlse = _oracle_full(w, want["sel_clean"])
     TL.assert_out_lse(out, lse, rout, rlse)
     TL.assert_grads(dq, dk, dv, rdq, rdk, rdv)
 
 
 FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
+SPREAD_CHUNKS = 256        # evenly spread (index head, chunk) pairs checked at full size
+HOT_CHUNK_CAP = 2100       # the hot row whose every chunk is checked has at most this many entries
+
+
+def _stack_rows(results):
+    """(token index, head index) of every checked row, and the oracle's
+    out [n, D], lse [n] and dq [n, D] of those rows."""
+    toks, heads, outs, lses, dqs = [], [], [], [], []
+    for tq, hs, o_, l_, q_ in results:
+        tt, hh = np.meshgrid(tq, hs, indexing="ij")
+        toks.append(tt.ravel())
+        heads.append(hh.ravel())
+        outs.append(o_.reshape(-1, o_.shape[-1]))
+        lses.append(l_.ravel())
+        dqs.append(q_.reshape(-1, q_.shape[-1]))
+    return (np.concatenate(toks), np.concatenate(heads), np.concatenate(outs), np.concatenate(lses),
+            np.concatenate(dqs))
+
+
+def _gpu_rows(x, toks, heads):
+    return x[torch.as_tensor(toks, device=x.device), torch.as_tensor(heads, device=x.device)].cpu()
 
 
 @pytest.mark.parametrize("name,dq_mode", [(n, B.DQ_RECOMPUTE) for n in FULL] +
@@ -141,6 +175,12 @@ FULL = ["single8k", "varlen8", "long64k", "zipf16k"]
                                                                 ("varlen8_b128", B.DQ_DS_BUFFER),
                                                                 ("long64k_b128", B.DQ_DS_BUFFER)])
 def test_full_size_configs_sampled(name, dq_mode):
+    """Full size, in the bench's launch configuration.  out / lse / dq on 256
+    evenly spread (index head, chunk) pairs plus every chunk of one hot CSR
+    row (the hottest of head 0 with at most 2100 entries); dk / dv on the
+    hottest CSR row of the workload (long64k: the forced block 0, selected by
+    all 8192 chunks of a head; zipf16k: block 0, about 2047 chunks) and on
+    two random rows, each complete (every selecting chunk evaluated)."""
     print(f"[case] full-size {name} dq_mode={dq_mode}", flush=True)
     if name.endswith("_b128"):   # the same workload at key block 128
         w = make_workload(name[:-len("_b128")], block=128)
@@ -154,33 +194,32 @@ def test_full_size_configs_sampled(name, dq_mode):
     out, lse, dq, dk, dv = TL.run_forward_backward(p, t, sched)
     del t
     lay = want["layout"]
-    rng = np.random.default_rng(7)
-    # sampled chunks: first, last, and random ones, every head
-    chunks = sorted({(int(rng.integers(w.num_kv_heads)), int(g)) for g in
-                     [0, lay.C - 1, *rng.integers(0, lay.C, size=10)]})
-    ref = O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block, w.scale,
-                              chunks=chunks)
-    rows = np.zeros((w.total_tokens, w.num_q_heads), dtype=bool)
-    for i, g in chunks:
-        d, qpos, _ = O.chunk_keys(lay, want["sel_clean"], i, g)
-        rows[np.ix_(int(lay.cu[d]) + qpos, np.arange(16 * i, 16 * i + 16))] = True
-    TL.assert_out_lse(out, lse, ref[4], ref[5], rows=rows)
-    TL.assert_grad("dq", dq, ref[0], rows=rows)
-    # sampled key blocks: every chunk selecting them is recomputed
+    sel_clean = want["sel_clean"]
     counts = np.diff(want["row_ptr"], axis=1)
-    cand = [(i, r) for i in range(w.num_kv_heads) for r in range(lay.R) if 0 < counts[i, r] <= 160]
-    picks = [cand[j] for j in rng.choice(len(cand), size=min(3, len(cand)), replace=False)]
+    # out / lse / dq
+    spread = [(j % w.num_kv_heads, int(g))
+              for j, g in enumerate(np.linspace(0, lay.C - 1, SPREAD_CHUNKS).round().astype(int))]
+    capped = np.where(counts[0] <= HOT_CHUNK_CAP, counts[0], -1)
+    hot = int(np.argmax(capped))
+    hot_chunks = O.chunks_selecting_block(want, 0, hot)
+    chunks = sorted(set(spread) | set(hot_chunks))
+    res = O.chunk_rows(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale, chunks)
+    toks, heads, rout, rlse, rdq = _stack_rows(res)
+    print(f"[case] {name}: {len(chunks)} chunks ({len(hot_chunks)} of row {hot}), {len(toks)} rows",
+          flush=True)
+    TL.assert_out_lse(_gpu_rows(out, toks, heads), _gpu_rows(lse, toks, heads), rout, rlse)
+    TL.assert_grad("dq", _gpu_rows(dq, toks, heads), rdq)
+    # dk / dv on the hottest row and two random rows
+    i_hot, r_hot = np.unravel_index(int(np.argmax(counts)), counts.shape)
+    rng = np.random.default_rng(7)
+    picks = [(int(i_hot), int(r_hot))] + [(int(rng.integers(w.num_kv_heads)), int(rng.integers(lay.R)))
+                                          for _ in range(2)]
     for i, r in picks:
-        sel_chunks = O.chunks_selecting_block(want, i, r)
-        ref = O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, want["sel_clean"], w.block,
-                                  w.scale, chunks=sel_chunks)
-        d = int(lay.row_doc[r])
-        b = r - int(lay.blk_off[d])
-        toks = int(lay.cu[d]) + np.arange(b * w.block, min((b + 1) * w.block, int(lay.lens[d])))
-        kv_rows = np.zeros((w.total_tokens, w.num_kv_heads), dtype=bool)
-        kv_rows[toks, i] = True
-        TL.assert_grad("dk", dk, ref[1], rows=kv_rows)
-        TL.assert_grad("dv", dv, ref[2], rows=kv_rows)
+        toks, gk, gv = O.key_block_grads(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale, i, r)
+        print(f"[case] {name}: dk/dv of head {i} row {r} ({int(counts[i, r])} chunks)", flush=True)
+        hk = np.full(len(toks), i)
+        TL.assert_grad("dk", _gpu_rows(dk, toks, hk), gk)
+        TL.assert_grad("dv", _gpu_rows(dv, toks, hk), gv)
     # properties at full size
     assert torch.isfinite(out).all() and torch.isfinite(dq).all()
     assert torch.isfinite(dk).all() and torch.isfinite(dv).all()

@@ -131,3 +131,24 @@ def test_walk_rule_exhaustive(num_sms):
     # the bound is also a bound for every smaller capacity
     for c2 in (0, 1, 100, 2399, 2400, 4999):
         assert O.grid_launch_bound(c2, num_sms) <= bound
+
+
+def test_golden_walks_with_tail():
+    """The tail split (tests/golden/walk_tail.json, hand-derived): walk
+    bounds of every case, and the page's bound n // r + s reached when the
+    tail has at least s rows (which only a tail spread over s walks does)."""
+    with open(os.path.join(GOLDEN, "walk_tail.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        n, s, r = case["n"], case["s"], case["r"]
+        assert O.rows_per_cta(n) == r
+        assert O.chunk_map(n, r, s) == tuple(case["chunk_map"])
+        full, tail, grid = case["chunk_map"]
+        walks = [O.walk_bounds(n, r, s, cta) for cta in range(grid)]
+        if "walks" in case:
+            assert walks == [tuple(x) for x in case["walks"]]
+        else:
+            assert walks[full:] == [tuple(x) for x in case["walks_tail"]]
+            assert walks[:full] == [(x * r, (x + 1) * r) for x in range(full)]
+        if tail >= s:
+            assert grid == n // r + s
