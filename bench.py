@@ -95,11 +95,10 @@ def cpu_baseline(w, sched_host, budget_s: float = 12.0) -> dict:
     backward of each), reported in useful TFLOP/s."""
     import numpy as np
     from oracle import msa_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    # the host cores this process may run on; the BLAS pool is pinned to that count
+    cores = len(os.sched_getaffinity(0))
+    from threadpoolctl import threadpool_limits
+    limiter = threadpool_limits(limits=cores)
     lay = sched_host["layout"]
     sel_clean = sched_host["sel_clean"]
     order = [(i, g) for g in np.linspace(0, lay.C - 1, 256).astype(int) for i in range(w.num_kv_heads)]
@@ -113,6 +112,7 @@ def cpu_baseline(w, sched_host, budget_s: float = 12.0) -> dict:
         if time.perf_counter() - t0 > budget_s and len(done) >= 8:
             break
     dt = time.perf_counter() - t0
+    limiter.unregister()
     return {"value": pairs * (fwd_f + bwd_f) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{len(done)} (index head, chunk) pairs of the {WORKLOAD} workload spread evenly "
@@ -276,6 +276,8 @@ def main() -> int:
               if per_kernel[kname] > 0 and f > 0}
     bwd_ms = per_kernel["bwd_pre"] + per_kernel["bwd_main"] + per_kernel["bwd_dq"] + per_kernel["bwd_post"]
     bwd_tflops = n_pairs * bwd_f / (bwd_ms * 1e-3) / 1e12
+    main_dq_ms = per_kernel["bwd_main"] + per_kernel["bwd_dq"]
+    main_dq_tflops = n_pairs * bwd_f / (main_dq_ms * 1e-3) / 1e12 if main_dq_ms > 0 else 0.0
     dominant_tflops = n_pairs * useful[dominant] / (dominant_ms * 1e-3) / 1e12 if dominant_ms > 0 else 0.0
 
     result = {
@@ -309,6 +311,10 @@ def main() -> int:
         "kernels_compulsory_GBps": {n: round(x, 1) for n, x in gbps.items()},
         "kernels_pct_hbm_peak": {n: round(100.0 * x / PEAK_HBM_GBS, 1) for n, x in gbps.items()},
         "forward_pct_peak": round(100.0 * tflops["forward"] / PEAK_BF16_TFLOPS, 2),
+        # the backward's five contractions per pair over the main and dQ kernels together
+        "bwd_main_plus_dq": {"ms": round(per_kernel["bwd_main"] + per_kernel["bwd_dq"], 4),
+                             "useful_tflops": round(main_dq_tflops, 2),
+                             "pct_peak": round(100.0 * main_dq_tflops / PEAK_BF16_TFLOPS, 2)},
         "backward_useful_tflops": round(bwd_tflops, 2),
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(dominant_tflops, 2), "peak": PEAK_BF16_TFLOPS,
