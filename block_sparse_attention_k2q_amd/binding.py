@@ -23,7 +23,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
-MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_HIP = range(6)
+(MSA_OK, MSA_ERR_INVALID, MSA_ERR_UNSUPPORTED, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_HIP,
+ MSA_ERR_SCRATCH_LIMIT) = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MSA_NOALLOC_SCRATCH_BYTES (msa.h)
 SCHED_ERR_DROPPED, SCHED_ERR_GEOMETRY = 0, 1
 DQ_RECOMPUTE, DQ_ATOMIC_POOL, DQ_DS_BUFFER, DQ_ATOMIC_POOL_BF16 = 0, 1, 2, 3
 MAX_DOC_CHUNKS = 1 << 18
@@ -34,7 +36,7 @@ EXPORTED = (
     "msa_device_check", "msa_schedule_layout_of", "msa_build_schedule", "msa_forward",
     "msa_backward_scratch_bytes", "msa_backward", "msa_backward_preprocess", "msa_backward_main",
     "msa_backward_dq", "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
-    "msa_index_scratch_bytes", "msa_index_select",
+    "msa_index_scratch_bytes", "msa_index_select", "msa_backward_noalloc",
 )
 
 
@@ -91,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "msa_index_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "msa_index_select": ([P, vp, vp, i32p, vp, i32p, vp], ctypes.c_int),
+            "msa_backward_noalloc": ([P, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(h, name)
@@ -106,7 +109,7 @@ def _check(status: int, what: str) -> None:
     msg = f"{what}: {lib().msa_status_string(status).decode()}"
     if status == MSA_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
-    if status in (MSA_ERR_INVALID, MSA_ERR_SHAPE, MSA_ERR_ALIGN):
+    if status in (MSA_ERR_INVALID, MSA_ERR_SHAPE, MSA_ERR_ALIGN, MSA_ERR_SCRATCH_LIMIT):
         raise ValueError(msg)
     raise RuntimeError(msg)
 
@@ -303,6 +306,22 @@ def msa_backward(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched, scratch
         _check(lib().msa_backward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
                                   _ptr(lse), _ptr(cu_seqlens), _ptr(sched), _ptr(scratch), _ptr(dq),
                                   _ptr(dk), _ptr(dv), _stream(stream)), "msa_backward")
+
+
+def msa_backward_noalloc(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched, dq, dk, dv,
+                         stream=None) -> None:
+    """msa_backward with the library's static scratch (allocates nothing;
+    ValueError when the problem needs more than NOALLOC_SCRATCH_BYTES)."""
+    _check_bwd_inputs(p, q, k, v, out, dout, lse, cu_seqlens, sched, None)
+    T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
+    _expect(dq, "dq", torch.bfloat16, (T, hq, D))
+    _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
+    _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
+    with _on_device(q, k, v, out, dout, lse, cu_seqlens, sched, dq, dk, dv):
+        ps = p.c_struct()
+        _check(lib().msa_backward_noalloc(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                          _ptr(lse), _ptr(cu_seqlens), _ptr(sched), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _stream(stream)), "msa_backward_noalloc")
 
 
 def msa_backward_preprocess(p: Problem, out, dout, scratch, stream=None) -> None:

@@ -211,6 +211,8 @@ const char* msa_status_string(int status) {
     case MSA_ERR_SHAPE: return "inconsistent sizes";
     case MSA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case MSA_ERR_HIP: return "HIP runtime error";
+    case MSA_ERR_SCRATCH_LIMIT:
+      return "problem needs more scratch than the static buffer of msa_backward_noalloc holds";
     default: return "unknown status";
   }
 }

@@ -45,7 +45,9 @@ typedef enum msa_status {
   MSA_ERR_UNSUPPORTED = 2,  /* device is not gfx950, or a size the kernels are not built for */
   MSA_ERR_SHAPE = 3,        /* sizes inconsistent with each other */
   MSA_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
-  MSA_ERR_HIP = 5           /* a HIP runtime call or launch failed */
+  MSA_ERR_HIP = 5,          /* a HIP runtime call or launch failed */
+  MSA_ERR_SCRATCH_LIMIT = 6 /* msa_backward_noalloc: the problem needs more scratch than
+                               MSA_NOALLOC_SCRATCH_BYTES */
 } msa_status;
 
 /* Problem geometry; all fields are host integers.  num_chunks, num_kblocks
@@ -169,6 +171,23 @@ int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
 int msa_backward(const msa_problem* p, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, const int32_t* cu_seqlens,
                  const int32_t* sched, void* scratch, void* dq, void* dk, void* dv, void* stream);
+
+/* msa_backward without the scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The scratch is a static device array of
+ * MSA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends; this call allocates nothing.  Arguments, layouts and the
+ * result are those of msa_backward.  Returns MSA_ERR_SCRATCH_LIMIT, before
+ * anything is enqueued, when msa_backward_scratch_bytes(p) exceeds the
+ * array (64 MiB: with dq_mode MSA_DQ_RECOMPUTE an 8K-token, 4 x 16-head,
+ * head-dim-128 problem needs 34 MiB; the MSA_DQ_DS_BUFFER slots alone need
+ * 16 KiB per selection slot, so that mode fits small problems only).  All
+ * calls on one GPU share its array: calls that overlap on one GPU race. */
+#define MSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int msa_backward_noalloc(const msa_problem* p, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse,
+                         const int32_t* cu_seqlens, const int32_t* sched, void* dq, void* dk,
+                         void* dv, void* stream);
 
 /* The steps of msa_backward, callable one at a time (same arguments and
  * scratch; used to time each kernel).  Order: preprocess, main, dq,
