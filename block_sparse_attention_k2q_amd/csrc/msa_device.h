@@ -258,13 +258,16 @@ __device__ __forceinline__ void stage_block(bf16* tile, const bf16* __restrict__
   constexpr int RPP = 64 / CPR;
   constexpr int N = kBlock / RPP / NWAVES;
   const bf16* first = src + ((int64_t)(tok0 + b * kBlock) * Hkv + i) * D;
-  const int kmax = len - 1 - b * kBlock;
+  // byte offsets: row * stride does not depend on the block (kept out of the
+  // block loop by the compiler), the clamp to the last key is one min.
+  const int stride = Hkv * D * 2;
+  const int kmax_off = (len - 1 - b * kBlock) * stride;
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const int piece = n * NWAVES + w;
     const int row = piece * RPP + lane / CPR;
     const int lc = (lane % CPR) ^ chunk_swizzle<CPR>(row);
-    const uint32_t o = (uint32_t)(min(row, kmax) * Hkv * D + 8 * lc) * 2u;
+    const uint32_t o = (uint32_t)(min(row * stride, kmax_off) + 16 * lc);
     dma16_at(first, o, tile + piece * 512);
   }
 }
