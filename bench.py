@@ -39,10 +39,13 @@ WORKLOAD = "single8k"
 KERNEL_FILES = {"forward": "forward.hip", "bwd_main": "backward.hip", "bwd_dq": "dq.hip"}
 KERNEL_FILES_RECOMPUTE = dict(KERNEL_FILES, bwd_dq="dq_recompute.hip")
 KERNEL_NAMES = {  # per dq mode
-    "recompute": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, false>",
+    "recompute": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, false, 1>",
                   "bwd_dq": "dq_kernel<128>"},
-    "ds": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true>",
+    "ds": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true, 1>",
            "bwd_dq": "dq_from_ds_kernel<128>"},
+    # key block 128: both 64-key tiles of a block in one 8-wave workgroup
+    "ds_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true, 2>",
+                "bwd_dq": "dq_from_ds_kernel<128>"},
     "atomic": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, false>"},
     "atomic_bf16": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
 }
@@ -253,6 +256,7 @@ def main() -> int:
 
     fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
     gemm = bwd_f // 5
+    names_key = "ds_b128" if args.block == 128 else args.dq_mode
     value = n_pairs * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     # useful contractions per pair done by each kernel
     pool = dq_mode in (B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16)
@@ -319,8 +323,8 @@ def main() -> int:
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(dominant_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dominant_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(dominant, args.dq_mode),
-                     "kernel": KERNEL_NAMES[args.dq_mode][dominant],
+                     "traffic": measured_traffic(dominant, names_key),
+                     "kernel": KERNEL_NAMES[names_key][dominant],
                      "launch_ms": round(dominant_ms, 4)},
     }
     # The index scorer (the step that produces the selection; not part of the

@@ -467,6 +467,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
 //    registers meanwhile) overwrites it for dK += dS^T Q; each wave owns
 //    2 (head dim 128) or 1 (head dim 64) of the 32 x 32 output tiles of dV
 //    and of dK.
+//
+// Key block 128 (KT = 2 key tiles of 64): one workgroup of 8 waves per walk
+// half, waves 4t .. 4t+3 doing the above for keys 64t .. 64t+63 of the
+// block, so both halves of the block share one gather of the Q / dO rows
+// (msa_schedule page: BLOCK_SIZE 128; msa_backward_sm100 page: TILE_N 128).
 // ---------------------------------------------------------------------------
 constexpr int kHalfM = kTileM / 2;
 
@@ -479,20 +484,20 @@ struct KvHalf {
 // Copy the Q / dO rows of one half task tile into a swizzled buffer.  Rows
 // past the document end read the chunk's last valid row (their
 // probabilities are forced to 0 by the consumer).
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__ q,
                                           const bf16* __restrict__ dout, const int* m, int half, int Hq,
                                           int w, int lane) {
   constexpr int CPR = D / 8;
   constexpr int RPP = 64 / CPR;                 // rows per wave-sized piece
   constexpr int PIECES = kHalfM / RPP;          // pieces per tensor
-  static_assert(PIECES % 4 == 0 && 16 % RPP == 0, "pieces split evenly over 4 waves, within a token");
+  static_assert(PIECES % NW == 0 && 16 % RPP == 0, "pieces split evenly over the waves, within a token");
   const int i = __builtin_amdgcn_readfirstlane(m[0]), qb = __builtin_amdgcn_readfirstlane(m[2]);
   const int qc = __builtin_amdgcn_readfirstlane(m[3]), tok0 = __builtin_amdgcn_readfirstlane(m[6]);
   const int lrow = lane / CPR, pcol = lane % CPR;
 #pragma unroll
-  for (int n = 0; n < PIECES / 4; ++n) {
-    const int piece = n * 4 + w;
+  for (int n = 0; n < PIECES / NW; ++n) {
+    const int piece = n * NW + w;
     const int row = piece * RPP + lrow;         // local row = (token - 4*half) * 16 + head
     // all rows of a piece belong to one token: a wave-uniform base per piece
     const int j = min(4 * half + ((piece * RPP) >> 4), qc - 1);
@@ -504,8 +509,8 @@ __device__ __forceinline__ void stage_qdo(KvHalf<D>& t, const bf16* __restrict__
   }
 }
 
-template <int D, bool WRITE_DS>
-__global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
+template <int D, bool WRITE_DS, int KT>
+__global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
@@ -517,22 +522,22 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
   constexpr int NT = D / 32;
   constexpr int OUT_TILES = 2 * NT / 4;        // dV (and dK) output tiles per wave
   static_assert(NT == 4 || NT == 2, "head dim 128 or 64");
+  static_assert(KT == 1 || KT == 2, "one or two 64-key tiles per workgroup");
+  constexpr int NW = 4 * KT;                   // waves
   // Separate objects, so the compiler can tell the copy into one buffer
   // from reads of the other (and of pd) and waits only where needed.
   __shared__ __attribute__((aligned(16))) KvHalf<D> tile0;
   __shared__ __attribute__((aligned(16))) KvHalf<D> tile1;
-  __shared__ __attribute__((aligned(16))) bf16 pd[kHalfM * kBlock];  // P^T, then dS^T (rows = queries)
-  __shared__ int meta[kMaxWalk][8];   // per walked task: i, r, qb, qc, d, b, tok0, len
+  // P^T, then dS^T, of each key tile (rows = queries)
+  __shared__ __attribute__((aligned(16))) bf16 pd_all[KT][kHalfM * kBlock];
+  // per walked task: i, r, qb, qc, dS slot of the first tile, first tile, tok0, len
+  __shared__ int meta[kMaxWalk][8];
 
   if (err[1]) return;
   const int grid_walks = desc[5];
-  // Key block 128 (sub = 2): workgroups x and x + 8 (same XCD, launched
-  // close together) take the two 64-key tiles of the same walk half, so
-  // the second gathers its Q / dO rows from the L2.
-  const int tsub = sub == 1 ? 0 : (blockIdx.x >> 3) & 1;
-  const int unit = sub == 1 ? blockIdx.x : ((blockIdx.x >> 4) << 3) | (blockIdx.x & 7);
-  const int wg = unit >> 1;
-  const int half = unit & 1;
+  // Workgroup 2x + half takes query half `half` of every task of walk x.
+  const int wg = blockIdx.x >> 1;
+  const int half = blockIdx.x & 1;
   if (wg >= grid_walks) return;
   const int rpc = desc[1], full = desc[2], tail = desc[3], tail_walks = desc[4];
   int lo, hi;
@@ -547,17 +552,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
   }
 
   const int w = wave_id(), lane = lane_id();
+  const int kt = KT == 1 ? 0 : w >> 2;         // this wave's 64-key tile of the block
+  const int wl = KT == 1 ? w : w & 3;          // its wave within that tile
+  bf16* const pd = pd_all[kt];
   const int n32 = lane & 31, h = lane >> 5;
   const int Hq = Hkv * kQPerKV;
   const float c2 = scale * kLog2e;
-  const int mq = 32 * (w & 1) + n32;           // this lane's query row in the half tile
-  const int kh = w >> 1;                       // this wave's 32-key half of the block
+  const int mq = 32 * (wl & 1) + n32;          // this lane's query row in the half tile
+  const int kh = wl >> 1;                      // this wave's 32-key half of the tile
   const int jtok = 4 * half + (mq >> 4);       // its token within the chunk
 
   int own_mt[OUT_TILES], own_nt[OUT_TILES];
 #pragma unroll
   for (int x = 0; x < OUT_TILES; ++x) {
-    const int tile = w * OUT_TILES + x;
+    const int tile = wl * OUT_TILES + x;
     own_nt[x] = tile / 2;
     own_mt[x] = tile % 2;
   }
@@ -589,12 +597,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
   };
 
   const int nrows = hi - lo;
-  for (int e = threadIdx.x; e < nrows; e += kBwdThreads) {
+  for (int e = threadIdx.x; e < nrows; e += kBwdThreads * KT) {
     const int32_t* tm = task_meta + (int64_t)(lo + e) * 6;
     int* m = meta[e];
 #pragma unroll
     for (int x = 0; x < 6; ++x) m[x] = tm[x];
-    m[5] = sub * tm[5] + tsub;   // this workgroup's 64-key tile of the block
+    m[5] = sub * tm[5];          // the block's first 64-key tile (a wave adds its kt)
     const int d = tm[4];
     const int t0 = cu[d];
     m[6] = t0;
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       const int32_t* sel = sel_clean + row * K;
       int slot = -1;
       for (int x = 0; x < K; ++x) slot = sel[x] == tm[5] ? x : slot;
-      m[4] = slot < 0 ? -1 : (int)((row * K + slot) * sub + tsub);
+      m[4] = slot < 0 ? -1 : (int)((row * K + slot) * sub);   // first tile's slot
     }
   }
   lds_barrier();
@@ -617,7 +625,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
   };
   float next_lse = 0.f, next_delta = 0.f;
   if (nrows > 0) {
-    stage_qdo<D>(tile0, q, dout, meta[0], half, Hq, w, lane);
+    stage_qdo<D, NW>(tile0, q, dout, meta[0], half, Hq, w, lane);
     next_lse = lse[row_index(meta[0])];
     next_delta = delta[row_index(meta[0])];
   }
@@ -629,7 +637,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     // wave-uniform task fields, kept in scalar registers
     const int i = __builtin_amdgcn_readfirstlane(mrow[0]), r = __builtin_amdgcn_readfirstlane(mrow[1]);
     const int qb = __builtin_amdgcn_readfirstlane(mrow[2]), qc = __builtin_amdgcn_readfirstlane(mrow[3]);
-    const int b = __builtin_amdgcn_readfirstlane(mrow[5]);
+    const int b = __builtin_amdgcn_readfirstlane(mrow[5]) + kt;
     const int tok0 = __builtin_amdgcn_readfirstlane(mrow[6]), len = __builtin_amdgcn_readfirstlane(mrow[7]);
     wait_vmem();
     lds_barrier();   // task e landed; every wave is done with task e-1 and with pd
@@ -657,13 +665,23 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
     }
     const float lv = next_lse, dl = next_delta;
     if (row + 1 < hi) {
-      stage_qdo<D>(N, q, dout, meta[e + 1], half, Hq, w, lane);
+      stage_qdo<D, NW>(N, q, dout, meta[e + 1], half, Hq, w, lane);
       next_lse = lse[row_index(meta[e + 1])];
       next_delta = delta[row_index(meta[e + 1])];
     }
-    // this half holds no token of the chunk, or the tile starts after the
-    // chunk's last query (second tile of a 128-key block: all keys masked)
-    if (4 * half >= qc || b * kBlock > qb + qc - 1) return;
+    // this half holds no token of the chunk (the same for every wave)
+    if (4 * half >= qc) return;
+    // this wave's tile starts after the chunk's last query (the second tile
+    // of a 128-key block: all keys masked); with one tile per workgroup it
+    // never happens (the selection keeps only blocks that start by then).
+    // The waves of the other tile go on, so the three barriers below are
+    // kept here.
+    if (b * kBlock > qb + qc - 1) {
+      lds_sync();
+      lds_sync();
+      lds_sync();
+      return;
+    }
 
     // --- S^T and dP^T: 32 keys x 32 queries per wave ---------------------------
     floatx16 st = floatx16{}, dpt = floatx16{};
@@ -717,11 +735,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void backward_kv_kernel(
       // 32-row block r of the tile and 16-key step u, 64 lanes x 8 bf16, lane
       // n + 32h' carrying row 32r + n, keys 16u + {0..3, 8..11} (h' = 0) or
       // 16u + {4..7, 12..15} (h' = 1).  This lane's row block is
-      // 2 half + (w & 1), its steps 2kh and 2kh + 1, and h' = h.
-      const int slot = __builtin_amdgcn_readfirstlane(mrow[4]);
-      if (slot >= 0) {
+      // 2 half + (wl & 1), its steps 2kh and 2kh + 1, and h' = h.
+      const int slot0 = __builtin_amdgcn_readfirstlane(mrow[4]);
+      if (slot0 >= 0) {
+        const int slot = slot0 + kt;
         bf16* dst = ds + (int64_t)slot * (kDsSlotBytes / 2) +
-                    ((2 * half + (w & 1)) * 4 + 2 * kh) * 512 + lane * 8;
+                    ((2 * half + (wl & 1)) * 4 + 2 * kh) * 512 + lane * 8;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           bf16x8 v8;
@@ -844,15 +863,11 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
     if (p.head_dim == 128) return go(backward_main_kernel<128, true>, sizeof(BwdSmem<128>));
     return go(backward_main_kernel<64, true>, sizeof(BwdSmem<64>));
   }
-  // Two workgroups per walk, one per query half of every task tile.
-  auto go_kv = [&](auto kern) {
+  // Two workgroups per walk, one per query half of every task tile; with
+  // key block 128 each holds both 64-key tiles of the block (8 waves).
+  auto go_kv = [&](auto kern, int kt) {
     const int sub = p.block_size / kBlock;
-    // Units u = 2 walk + half; with two tiles per block, tile t of unit u is
-    // workgroup ((u >> 3) << 4) | (t << 3) | (u & 7), so the launch rounds the
-    // units up to whole groups of eight (units past the walks return at once).
-    const int64_t units = 2 * grid;
-    const int64_t nwg = sub == 1 ? units : (units + 7) / 8 * 16;
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kBwdThreads), 0, stream, (const bf16*)q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads * kt), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
@@ -860,12 +875,16 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        p.num_kv_heads, p.num_chunks, p.topk, sub, p.softmax_scale);
     return hipGetLastError();
   };
-  if (p.dq_mode == MSA_DQ_DS_BUFFER) {
-    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true>);
-    return go_kv(backward_kv_kernel<64, true>);
+  if (p.block_size == 128) {   // dS-buffer mode only (checked at the boundary)
+    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true, 2>, 2);
+    return go_kv(backward_kv_kernel<64, true, 2>, 2);
   }
-  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, false>);
-  return go_kv(backward_kv_kernel<64, false>);
+  if (p.dq_mode == MSA_DQ_DS_BUFFER) {
+    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true, 1>, 1);
+    return go_kv(backward_kv_kernel<64, true, 1>, 1);
+  }
+  if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, false, 1>, 1);
+  return go_kv(backward_kv_kernel<64, false, 1>, 1);
 }
 
 hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
