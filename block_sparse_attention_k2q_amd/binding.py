@@ -36,7 +36,7 @@ EXPORTED = (
     "msa_device_check", "msa_schedule_layout_of", "msa_build_schedule", "msa_forward",
     "msa_backward_scratch_bytes", "msa_backward", "msa_backward_preprocess", "msa_backward_main",
     "msa_backward_dq", "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
-    "msa_index_scratch_bytes", "msa_index_select", "msa_backward_noalloc",
+    "msa_index_scratch_bytes", "msa_index_select", "msa_backward_noalloc", "msa_build_schedule_kv",
 )
 
 
@@ -48,12 +48,12 @@ class MSAProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "total_tokens", "num_docs", "num_kv_heads", "q_per_kv", "head_dim", "block_size",
         "query_chunk", "topk", "num_chunks", "num_kblocks", "max_doc_chunks", "num_cus")] + [
-        ("softmax_scale", ctypes.c_float), ("dq_mode", ctypes.c_int32)]
+        ("softmax_scale", ctypes.c_float), ("dq_mode", ctypes.c_int32), ("kv_rows", ctypes.c_int32)]
 
 
 class MSAScheduleLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
-        "desc", "err", "doc_chunk_off", "doc_blk_off", "chunk_doc", "sel_clean", "row_cursor",
+        "desc", "err", "doc_chunk_off", "doc_blk_off", "doc_kv_off", "chunk_doc", "sel_clean", "row_cursor",
         "row_ptr", "head_off", "q_idx", "task_meta", "total")]
 
 
@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "msa_device_check": ([ctypes.c_int, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
             "msa_schedule_layout_of": ([P, ctypes.POINTER(MSAScheduleLayout)], ctypes.c_int),
             "msa_build_schedule": ([P, i32p, i32p, i32p, vp], ctypes.c_int),
+            "msa_build_schedule_kv": ([P, i32p, i32p, i32p, i32p, vp], ctypes.c_int),
             "msa_forward": ([P, vp, vp, vp, i32p, i32p, vp, vp, vp], ctypes.c_int),
             "msa_backward_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "msa_backward": ([P, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp, vp, vp], ctypes.c_int),
@@ -147,11 +148,12 @@ class Problem:
     block_size: int = 64
     query_chunk: int = 8
     dq_mode: int = DQ_DS_BUFFER
+    kv_rows: int = 0           # rows of k, v, dk, dv; 0 = total_tokens (compact)
 
     @staticmethod
     def make(cu_seqlens, num_kv_heads: int, head_dim: int, topk: int, num_cus: int = 256,
              softmax_scale: Optional[float] = None, block_size: int = 64,
-             dq_mode: int = DQ_DS_BUFFER) -> "Problem":
+             dq_mode: int = DQ_DS_BUFFER, kv_rows: int = 0) -> "Problem":
         cu = np.asarray(cu_seqlens, dtype=np.int64)
         lens = np.diff(cu)
         nch = -(-lens // 8)
@@ -160,11 +162,16 @@ class Problem:
                        num_kblocks=int((-(-lens // block_size)).sum()),
                        max_doc_chunks=int(nch.max(initial=0)), num_cus=int(num_cus),
                        softmax_scale=float(head_dim ** -0.5 if softmax_scale is None else softmax_scale),
-                       block_size=int(block_size), dq_mode=int(dq_mode))
+                       block_size=int(block_size), dq_mode=int(dq_mode), kv_rows=int(kv_rows))
 
     @property
     def num_q_heads(self) -> int:
         return self.num_kv_heads * self.q_per_kv
+
+    @property
+    def kv_total(self) -> int:
+        """Rows of k, v, dk, dv."""
+        return self.kv_rows if self.kv_rows > 0 else self.total_tokens
 
     @property
     def capacity(self) -> int:
@@ -174,7 +181,7 @@ class Problem:
         return MSAProblem(self.total_tokens, self.num_docs, self.num_kv_heads, self.q_per_kv,
                           self.head_dim, self.block_size, self.query_chunk, self.topk,
                           self.num_chunks, self.num_kblocks, self.max_doc_chunks, self.num_cus,
-                          self.softmax_scale, self.dq_mode)
+                          self.softmax_scale, self.dq_mode, self.kv_rows)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -228,9 +235,25 @@ def msa_build_schedule(p: Problem, cu_seqlens: torch.Tensor, sel: torch.Tensor, 
                                         _stream(stream)), "msa_build_schedule")
 
 
+def msa_build_schedule_kv(p: Problem, cu_seqlens: torch.Tensor, sel: torch.Tensor,
+                          kv_starts: Optional[torch.Tensor], sched: torch.Tensor, stream=None) -> None:
+    """msa_build_schedule with each document's keys at row kv_starts[d] of
+    k / v (int32 [num_docs] on the device; None = the cu_seqlens rows)."""
+    L = msa_schedule_layout_of(p)
+    _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
+    _expect(sel, "sel", torch.int32, (p.num_kv_heads, p.num_chunks, p.topk))
+    _expect(sched, "sched", torch.int32, (L.total,))
+    if kv_starts is not None:
+        _expect(kv_starts, "kv_starts", torch.int32, (p.num_docs,))
+    with _on_device(cu_seqlens, sel, sched, kv_starts):
+        ps = p.c_struct()
+        _check(lib().msa_build_schedule_kv(ctypes.byref(ps), _ptr(cu_seqlens), _ptr(sel), _ptr(kv_starts),
+                                           _ptr(sched), _stream(stream)), "msa_build_schedule_kv")
+
+
 def msa_forward(p: Problem, q, k, v, cu_seqlens, sched, out, lse, stream=None) -> None:
-    T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
-    for name, t, shape in (("q", q, (T, hq, D)), ("k", k, (T, hkv, D)), ("v", v, (T, hkv, D)),
+    T, hq, hkv, D, W = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim, p.kv_total
+    for name, t, shape in (("q", q, (T, hq, D)), ("k", k, (W, hkv, D)), ("v", v, (W, hkv, D)),
                            ("out", out, (T, hq, D))):
         _expect(t, name, torch.bfloat16, shape)
     _expect(lse, "lse", torch.float32, (T, hq))
@@ -279,8 +302,8 @@ def msa_backward_scratch_bytes(p: Problem) -> int:
 
 
 def _check_bwd_inputs(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched, scratch):
-    T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
-    for name, t, shape in (("q", q, (T, hq, D)), ("k", k, (T, hkv, D)), ("v", v, (T, hkv, D)),
+    T, hq, hkv, D, W = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim, p.kv_total
+    for name, t, shape in (("q", q, (T, hq, D)), ("k", k, (W, hkv, D)), ("v", v, (W, hkv, D)),
                            ("out", out, (T, hq, D)), ("dout", dout, (T, hq, D))):
         if t is not None:
             _expect(t, name, torch.bfloat16, shape)
@@ -299,8 +322,8 @@ def msa_backward(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched, scratch
     _check_bwd_inputs(p, q, k, v, out, dout, lse, cu_seqlens, sched, scratch)
     T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
-    _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
-    _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
+    _expect(dk, "dk", torch.bfloat16, (p.kv_total, hkv, D))
+    _expect(dv, "dv", torch.bfloat16, (p.kv_total, hkv, D))
     with _on_device(q, k, v, out, dout, lse, cu_seqlens, sched, scratch, dq, dk, dv):
         ps = p.c_struct()
         _check(lib().msa_backward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
@@ -315,8 +338,8 @@ def msa_backward_noalloc(p: Problem, q, k, v, out, dout, lse, cu_seqlens, sched,
     _check_bwd_inputs(p, q, k, v, out, dout, lse, cu_seqlens, sched, None)
     T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
-    _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
-    _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
+    _expect(dk, "dk", torch.bfloat16, (p.kv_total, hkv, D))
+    _expect(dv, "dv", torch.bfloat16, (p.kv_total, hkv, D))
     with _on_device(q, k, v, out, dout, lse, cu_seqlens, sched, dq, dk, dv):
         ps = p.c_struct()
         _check(lib().msa_backward_noalloc(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
@@ -356,8 +379,8 @@ def msa_backward_postprocess(p: Problem, scratch, dq, dk, dv, stream=None) -> No
     _check_bwd_inputs(p, None, None, None, None, None, None, None, None, scratch)
     T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
-    _expect(dk, "dk", torch.bfloat16, (T, hkv, D))
-    _expect(dv, "dv", torch.bfloat16, (T, hkv, D))
+    _expect(dk, "dk", torch.bfloat16, (p.kv_total, hkv, D))
+    _expect(dv, "dv", torch.bfloat16, (p.kv_total, hkv, D))
     with _on_device(scratch, dq, dk, dv):
         ps = p.c_struct()
         _check(lib().msa_backward_postprocess(ctypes.byref(ps), _ptr(scratch), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -389,6 +412,7 @@ def schedule_views(p: Problem, sched: torch.Tensor) -> dict:
         desc=sched[L.desc:L.desc + 8], err=sched[L.err:L.err + 8],
         doc_chunk_off=sched[L.doc_chunk_off:L.doc_chunk_off + p.num_docs + 1],
         doc_blk_off=sched[L.doc_blk_off:L.doc_blk_off + p.num_docs + 1],
+        doc_kv_off=sched[L.doc_kv_off:L.doc_kv_off + p.num_docs],
         chunk_doc=sched[L.chunk_doc:L.chunk_doc + C],
         sel_clean=sched[L.sel_clean:L.sel_clean + cap].view(hkv, C, K),
         row_ptr=sched[L.row_ptr:L.row_ptr + hkv * (R + 1)].view(hkv, R + 1),

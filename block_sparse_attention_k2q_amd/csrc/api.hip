@@ -24,7 +24,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_problem(const msa_problem* p) {
   if (!p) return MSA_ERR_INVALID;
   if (p->total_tokens < 0 || p->num_docs < 1 || p->num_kv_heads < 1 || p->topk < 1 ||
-      p->num_chunks < 0 || p->num_kblocks < 0 || p->max_doc_chunks < 0 || p->num_cus < 1)
+      p->num_chunks < 0 || p->num_kblocks < 0 || p->max_doc_chunks < 0 || p->num_cus < 1 ||
+      p->kv_rows < 0)
     return MSA_ERR_INVALID;
   if (p->q_per_kv != 16 || (p->block_size != 64 && p->block_size != 128) || p->query_chunk != 8 ||
       (p->head_dim != 64 && p->head_dim != 128) || p->topk > 64 ||
@@ -41,7 +42,8 @@ int check_problem(const msa_problem* p) {
   // Geometry implied by the sizes themselves.
   if ((int64_t)p->num_chunks * 8 < p->total_tokens || (int64_t)p->num_kblocks * p->block_size < p->total_tokens ||
       p->num_chunks > p->total_tokens || p->num_kblocks > p->num_chunks ||
-      p->max_doc_chunks > p->num_chunks || (p->num_chunks > 0 && p->max_doc_chunks < 1))
+      p->max_doc_chunks > p->num_chunks || (p->num_chunks > 0 && p->max_doc_chunks < 1) ||
+      (p->kv_rows > 0 && p->kv_rows < p->total_tokens))
     return MSA_ERR_SHAPE;
   if (!(p->softmax_scale > 0.f)) return MSA_ERR_INVALID;
   if (p->dq_mode != MSA_DQ_RECOMPUTE && p->dq_mode != MSA_DQ_ATOMIC_POOL &&
@@ -78,14 +80,20 @@ int msa_schedule_layout_of(const msa_problem* p, msa_schedule_layout* out) {
   return MSA_OK;
 }
 
-int msa_build_schedule(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
-                       int32_t* sched, void* stream) {
+int msa_build_schedule_kv(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
+                          const int32_t* kv_starts, int32_t* sched, void* stream) {
   const int st = check_problem(p);
   if (st != MSA_OK) return st;
   if (!cu_seqlens || !sched || (!sel && p->num_chunks > 0)) return MSA_ERR_INVALID;
   if (!aligned16(sched)) return MSA_ERR_ALIGN;
   const msa_schedule_layout L = msa::schedule_layout(*p);
-  return hip_status(msa::launch_build_schedule(*p, cu_seqlens, sel, sched, L, (hipStream_t)stream));
+  return hip_status(
+      msa::launch_build_schedule(*p, cu_seqlens, sel, kv_starts, sched, L, (hipStream_t)stream));
+}
+
+int msa_build_schedule(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
+                       int32_t* sched, void* stream) {
+  return msa_build_schedule_kv(p, cu_seqlens, sel, nullptr, sched, stream);
 }
 
 int msa_forward(const msa_problem* p, const void* q, const void* k, const void* v,

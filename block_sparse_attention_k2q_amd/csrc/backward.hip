@@ -136,7 +136,7 @@ struct BwdSmem {
   bf16 ds[kTileM * LDP];
   float lse2[kTileM];
   float delta[kTileM];
-  int meta[kMaxWalk][8];   // per walked task: i, r, qb, qc, d, b, tok0, len
+  int meta[kMaxWalk][9];   // per walked task: i, r, qb, qc, d, b, tok0, len, first K/V row of d
 };
 
 template <int D, bool BF16_POOL>
@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, void* __restrict__ dq_pool,
-    float* __restrict__ dk_acc, float* __restrict__ dv_acc, int Hkv, float scale) {
+    float* __restrict__ dk_acc, float* __restrict__ dv_acc, const int32_t* __restrict__ doc_kv_off, int Hkv,
+    float scale) {
   using S = BwdSmem<D>;
   constexpr int LDK = S::LDK, LDP = S::LDP;
   constexpr int KS = D / 16;                 // k steps over d
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
   }
   floatx16 acc_dv[OUT_TILES], acc_dk[OUT_TILES];
 
-  int cur_i = -1, cur_r = -1, cur_tok0 = 0, cur_len = 0, cur_b = 0;
+  int cur_i = -1, cur_r = -1, cur_kv0 = 0, cur_len = 0, cur_b = 0;
 
   auto flush = [&]() {
 #pragma unroll
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
         // P); they are sent to the block's first key so the atomics need no branch.
         const int key = 32 * own_mt[x] + 8 * (j >> 2) + 4 * h + (j & 3);
         const int kpos = cur_b * kBlock + (cur_b * kBlock + key < cur_len ? key : 0);
-        const int64_t off = ((int64_t)(cur_tok0 + kpos) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
+        const int64_t off = ((int64_t)(cur_kv0 + kpos) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
         atomicAdd(dv_acc + off, acc_dv[x][j]);
         atomicAdd(dk_acc + off, acc_dk[x][j]);
       }
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const int t0 = cu[d];
     m[6] = t0;
     m[7] = cu[d + 1] - t0;
+    m[8] = doc_kv_off[d];
   }
   lds_barrier();
 
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
   for (int row = lo; row < hi; ++row) {
     const int* mrow = sm.meta[row - lo];
     const int i = mrow[0], r = mrow[1], qb = mrow[2], qc = mrow[3], b = mrow[5];
-    const int tok0 = mrow[6], len = mrow[7];
+    const int tok0 = mrow[6], len = mrow[7], kv0 = mrow[8];
     lds_barrier();  // previous tile fully consumed
     if (i != cur_i || r != cur_r) {
       if (cur_i >= 0) flush();
@@ -261,13 +263,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
         acc_dv[x] = floatx16{};
         acc_dk[x] = floatx16{};
       }
-      cur_i = i; cur_r = r; cur_tok0 = tok0; cur_len = len; cur_b = b;
+      cur_i = i; cur_r = r; cur_kv0 = kv0; cur_len = len; cur_b = b;
       for (int e = threadIdx.x; e < kBlock * VEC; e += kBwdThreads) {
         const int kr = e / VEC, col = (e % VEC) * 8;
         const int kpos = b * kBlock + kr;
         u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
         if (kpos < len) {
-          const int64_t off = ((int64_t)(tok0 + kpos) * Hkv + i) * D + col;
+          const int64_t off = ((int64_t)(kv0 + kpos) * Hkv + i) * D + col;
           kv = *reinterpret_cast<const u32x4*>(k + off);
           vv = *reinterpret_cast<const u32x4*>(v + off);
         }
@@ -516,7 +518,8 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, float* __restrict__ dk_acc,
     float* __restrict__ dv_acc, bf16* __restrict__ ds, const int32_t* __restrict__ doc_chunk_off,
-    const int32_t* __restrict__ sel_clean, int Hkv, int C, int K, int sub, float scale) {
+    const int32_t* __restrict__ doc_kv_off, const int32_t* __restrict__ sel_clean, int Hkv, int C, int K,
+    int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -530,8 +533,9 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
   __shared__ __attribute__((aligned(16))) KvHalf<D> tile1;
   // P^T, then dS^T, of each key tile (rows = queries)
   __shared__ __attribute__((aligned(16))) bf16 pd_all[KT][kHalfM * kBlock];
-  // per walked task: i, r, qb, qc, dS slot of the first tile, first tile, tok0, len
-  __shared__ int meta[kMaxWalk][8];
+  // per walked task: i, r, qb, qc, dS slot of the first tile, first tile, tok0, len,
+  // first K/V row of the document
+  __shared__ int meta[kMaxWalk][9];
 
   if (err[1]) return;
   const int grid_walks = desc[5];
@@ -571,7 +575,7 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
   }
   floatx16 acc_dv[OUT_TILES], acc_dk[OUT_TILES];
   bf16x8 ka[KS], va[KS];                       // K, V rows of this wave's keys as MFMA A operands
-  int cur_i = -1, cur_r = -1, cur_tok0 = 0, cur_len = 0, cur_b = 0;
+  int cur_i = -1, cur_r = -1, cur_kv0 = 0, cur_len = 0, cur_b = 0;
 
   auto flush = [&]() {
     // Partial dK/dV of the finished bucket segment; keys past the document
@@ -582,7 +586,7 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
     for (int x = 0; x < OUT_TILES; ++x) {
       int kb = 32 * own_mt[x] + 4 * h;
       asm volatile("" : "+v"(kb));   // keep the per-register offsets below out of the task loop
-      const int64_t first = ((int64_t)(cur_tok0 + cur_b * kBlock) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
+      const int64_t first = ((int64_t)(cur_kv0 + cur_b * kBlock) * Hkv + cur_i) * D + 32 * own_nt[x] + n32;
       float* dvp = dv_acc + first;
       float* dkp = dk_acc + first;
       const int room = cur_len - cur_b * kBlock - kb;   // c_j < room: key inside the document
@@ -607,6 +611,7 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
     const int t0 = cu[d];
     m[6] = t0;
     m[7] = cu[d + 1] - t0;
+    m[8] = doc_kv_off[d];
     if constexpr (WRITE_DS) {
       // dS slot of the tile: (index head, global chunk, position of its block
       // in the chunk's cleaned selection, tile); the document id is not
@@ -638,7 +643,8 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
     const int i = __builtin_amdgcn_readfirstlane(mrow[0]), r = __builtin_amdgcn_readfirstlane(mrow[1]);
     const int qb = __builtin_amdgcn_readfirstlane(mrow[2]), qc = __builtin_amdgcn_readfirstlane(mrow[3]);
     const int b = __builtin_amdgcn_readfirstlane(mrow[5]) + kt;
-    const int tok0 = __builtin_amdgcn_readfirstlane(mrow[6]), len = __builtin_amdgcn_readfirstlane(mrow[7]);
+    const int len = __builtin_amdgcn_readfirstlane(mrow[7]);
+    const int kv0 = __builtin_amdgcn_readfirstlane(mrow[8]);
     wait_vmem();
     lds_barrier();   // task e landed; every wave is done with task e-1 and with pd
 
@@ -649,11 +655,11 @@ __global__ __launch_bounds__(kBwdThreads * KT, 2 / KT) void backward_kv_kernel(
         acc_dv[x] = floatx16{};
         acc_dk[x] = floatx16{};
       }
-      cur_i = i; cur_r = r; cur_tok0 = tok0; cur_len = len; cur_b = b;
+      cur_i = i; cur_r = r; cur_kv0 = kv0; cur_len = len; cur_b = b;
       // K, V row 32*kh + n32 of the block, d = 16s + 8h .. +7 (keys past the
       // document end read its last key; they are masked).
       const int key = min(b * kBlock + 32 * kh + n32, len - 1);
-      const int64_t off = ((int64_t)(tok0 + key) * Hkv + i) * D + 8 * h;
+      const int64_t off = ((int64_t)(kv0 + key) * Hkv + i) * D + 8 * h;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         ka[s] = load_bf16x8(k + off + 16 * s);
@@ -852,7 +858,7 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (void*)(base + S.dq_pool), (float*)(base + S.dk_acc),
-                       (float*)(base + S.dv_acc), p.num_kv_heads, p.softmax_scale);
+                       (float*)(base + S.dv_acc), sched + L.doc_kv_off, p.num_kv_heads, p.softmax_scale);
     return hipGetLastError();
   };
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) {
@@ -871,7 +877,7 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (float*)(base + S.dk_acc), (float*)(base + S.dv_acc),
-                       (bf16*)(base + S.ds), sched + L.doc_chunk_off, sched + L.sel_clean,
+                       (bf16*)(base + S.ds), sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean,
                        p.num_kv_heads, p.num_chunks, p.topk, sub, p.softmax_scale);
     return hipGetLastError();
   };
@@ -894,7 +900,7 @@ hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch
   const int64_t hq = (int64_t)p.num_kv_heads * p.q_per_kv;
   const int64_t n_q_vec =
       p.dq_mode == MSA_DQ_ATOMIC_POOL ? (int64_t)p.total_tokens * hq * p.head_dim / 8 : 0;
-  const int64_t n_kv_vec = (int64_t)p.total_tokens * p.num_kv_heads * p.head_dim / 8;
+  const int64_t n_kv_vec = kv_rows_of(p) * p.num_kv_heads * p.head_dim / 8;
   const int64_t n = n_q_vec > n_kv_vec ? n_q_vec : n_kv_vec;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(postprocess_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,

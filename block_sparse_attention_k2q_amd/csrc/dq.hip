@@ -30,7 +30,8 @@ template <int D>
 __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ ds, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ chunk_doc, const int32_t* __restrict__ doc_chunk_off,
-    const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ dq,
+    const int32_t* __restrict__ doc_kv_off, const int32_t* __restrict__ sel_clean,
+    const int32_t* __restrict__ err, bf16* __restrict__ dq,
     int Hkv, int C, int K, int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int NT = D / 32;
@@ -52,6 +53,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
   const int c = g - doc_chunk_off[d];
   const int tok0 = cu[d];
   const int len = cu[d + 1] - tok0;
+  const int kv0 = doc_kv_off[d];       // the document's first row of k
   const int p0 = kChunk * c;
   const int qcount = min(kChunk, len - p0);
   const int Hq = Hkv * kQPerKV;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
   const int nblk = s_n;
   bf16x8 d0[4], d1[4], d2[4];
   auto issue = [&](int n, bf16* kb, bf16x8 (&dst)[4]) {
-    stage_block<D, NW>(kb, k, tok0, len, s_block[n], Hkv, i, w, lane);
+    stage_block<D, NW>(kb, k, kv0, len, s_block[n], Hkv, i, w, lane);
     const bf16* src = ds_lane + (int64_t)s_slot[n] * (kDsSlotBytes / 2);
 #pragma unroll
     for (int u = 0; u < 4; ++u) dst[u] = load_bf16x8_stream(src + 512 * u);
@@ -146,7 +148,8 @@ hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k
     auto go_ds = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)k,
                          (const bf16*)((const uint8_t*)scratch + S.ds), cu, sched + L.chunk_doc,
-                         sched + L.doc_chunk_off, sched + L.sel_clean, sched + L.err, (bf16*)dq,
+                         sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean, sched + L.err,
+                         (bf16*)dq,
                          p.num_kv_heads, p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
     };
     if (p.head_dim == 128) go_ds(dq_from_ds_kernel<128>);

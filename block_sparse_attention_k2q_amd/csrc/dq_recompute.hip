@@ -33,8 +33,9 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
-    const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
-    const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv, int C, int K, float scale) {
+    const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_kv_off,
+    const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv,
+    int C, int K, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -51,6 +52,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
   const int c = g - doc_chunk_off[d];
   const int tok0 = cu[d];
   const int len = cu[d + 1] - tok0;
+  const int kv0 = doc_kv_off[d];       // the document's first row of k and v
   const int p0 = kChunk * c;
   const int qcount = min(kChunk, len - p0);
   const int Hq = Hkv * kQPerKV;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
 
   lds_barrier();
   const int nblk = s_nblocks;
-  if (nblk > 0) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[0], Hkv, i, w, lane);
+  if (nblk > 0) stage_kv<D, NW>(buf0, k, v, kv0, len, s_blocks[0], Hkv, i, w, lane);
 
   auto consume = [&](const KVTiles<D>& t, int b) {
     // S^T = K Q^T and dP^T = V dO^T, operands of step s+1 read during step s.
@@ -160,12 +162,12 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
     // Even blocks use buf0, odd blocks buf1.
     wait_vmem();
     lds_barrier();   // block bi landed in buf0; all waves are done with buf1
-    if (bi + 1 < nblk) stage_kv<D, NW>(buf1, k, v, tok0, len, s_blocks[bi + 1], Hkv, i, w, lane);
+    if (bi + 1 < nblk) stage_kv<D, NW>(buf1, k, v, kv0, len, s_blocks[bi + 1], Hkv, i, w, lane);
     consume(buf0, s_blocks[bi]);
     if (bi + 1 < nblk) {
       wait_vmem();
       lds_barrier();  // block bi+1 landed in buf1; all waves are done with buf0
-      if (bi + 2 < nblk) stage_kv<D, NW>(buf0, k, v, tok0, len, s_blocks[bi + 2], Hkv, i, w, lane);
+      if (bi + 2 < nblk) stage_kv<D, NW>(buf0, k, v, kv0, len, s_blocks[bi + 2], Hkv, i, w, lane);
       consume(buf1, s_blocks[bi + 1]);
     }
   }
@@ -197,7 +199,8 @@ hipError_t launch_dq_recompute(const msa_problem& p, const void* q, const void* 
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta, cu,
-                       sched + L.chunk_doc, sched + L.doc_chunk_off, sched + L.sel_clean, sched + L.err,
+                       sched + L.chunk_doc, sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean,
+                       sched + L.err,
                        (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
   };
   if (p.head_dim == 128) go(dq_kernel<128>);

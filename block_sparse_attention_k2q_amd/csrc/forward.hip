@@ -66,8 +66,9 @@ template <int D>
 __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
-    const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ sel_clean,
-    const int32_t* __restrict__ err, bf16* __restrict__ out, float* __restrict__ lse, int Hkv, int C,
+    const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_kv_off,
+    const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ out,
+    float* __restrict__ lse, int Hkv, int C,
     int K, int sub, float scale) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
@@ -92,6 +93,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
   const int c = g - doc_chunk_off[d];
   const int tok0 = cu[d];
   const int len = cu[d + 1] - tok0;
+  const int kv0 = doc_kv_off[d];       // the document's first row of k and v
   const int p0 = kChunk * c;
   const int qcount = min(kChunk, len - p0);
   const int Hq = Hkv * kQPerKV;
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
   const float c2 = scale * kLog2e;
 
   auto copy = [&](bf16* tile, const bf16* src, int b) {
-    stage_block<D, NW>(tile, src, tok0, len, b, Hkv, i, w, lane);
+    stage_block<D, NW>(tile, src, kv0, len, b, Hkv, i, w, lane);
   };
   // Issue order K0, V0, K1, then per step V_{j+1}, K_{j+2}: when block j is
   // due, only K_{j+1}'s copies may still be outstanding.
@@ -346,7 +348,8 @@ hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, co
   auto args = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(threads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, cu, sched + L.chunk_doc, sched + L.doc_chunk_off,
-                       sched + L.sel_clean, sched + L.err, (bf16*)out, lse, p.num_kv_heads,
+                       sched + L.doc_kv_off, sched + L.sel_clean, sched + L.err, (bf16*)out, lse,
+                       p.num_kv_heads,
                        p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
   };
   if (p.head_dim == 128) args(forward_kernel<128>, kFwdThreads);

@@ -36,6 +36,7 @@ inline msa_schedule_layout schedule_layout(const msa_problem& p) {
   o = align64(o);
   L.doc_chunk_off = o; o = align64(o + p.num_docs + 1);
   L.doc_blk_off = o; o = align64(o + p.num_docs + 1);
+  L.doc_kv_off = o; o = align64(o + p.num_docs);
   L.chunk_doc = o; o = align64(o + C);
   L.sel_clean = o; o = align64(o + cap);
   L.row_cursor = o; o = align64(o + kCounterCopies * hkv * R);
@@ -59,15 +60,18 @@ inline int64_t grid_launch_bound(int64_t cap, int num_cus) {
 struct BackwardScratch {
   size_t delta, dk_acc, dv_acc, dq_pool, ds, total;
 };
+// Rows of k, v, dk, dv (msa.h: kv_rows, 0 = compact).
+inline int64_t kv_rows_of(const msa_problem& p) { return p.kv_rows > 0 ? p.kv_rows : p.total_tokens; }
+
 inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t T = (size_t)p.total_tokens, hq = (size_t)p.num_kv_heads * p.q_per_kv,
-               hkv = (size_t)p.num_kv_heads, D = (size_t)p.head_dim;
+               hkv = (size_t)p.num_kv_heads, D = (size_t)p.head_dim, W = (size_t)kv_rows_of(p);
   BackwardScratch s;
   size_t o = 0;
   s.delta = o; o = a256(o + 4 * T * hq);
-  s.dk_acc = o; o = a256(o + 4 * T * hkv * D);
-  s.dv_acc = o; o = a256(o + 4 * T * hkv * D);
+  s.dk_acc = o; o = a256(o + 4 * W * hkv * D);
+  s.dv_acc = o; o = a256(o + 4 * W * hkv * D);
   s.dq_pool = o;
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) o = a256(o + 4 * T * hq * D);
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) o = a256(o + 2 * T * hq * D);
@@ -104,7 +108,8 @@ hipError_t launch_index_select(const msa_problem& p, const void* qi, const void*
                                void* scratch, int32_t* sel, hipStream_t stream);
 
 hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const int32_t* sel,
-                                 int32_t* sched, const msa_schedule_layout& L, hipStream_t stream);
+                                 const int32_t* kv_starts, int32_t* sched, const msa_schedule_layout& L,
+                                 hipStream_t stream);
 hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, const void* v,
                           const int32_t* cu, const int32_t* sched, const msa_schedule_layout& L,
                           void* out, float* lse, hipStream_t stream);

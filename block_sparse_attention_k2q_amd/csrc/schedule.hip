@@ -8,9 +8,9 @@
 // page (msa_task_build mirrors the walk rule on the device).
 //
 // Pipeline, all on one stream, no host synchronisation:
-//   geometry   workgroup 0: per-document chunk/block offsets, checks them
-//              against the host sizes, clears the error words; the other
-//              workgroups clear the row counters.
+//   geometry   workgroup 0: per-document chunk/block offsets and K/V start
+//              rows, checks them against the host sizes, clears the error
+//              words; the other workgroups clear the row counters.
 //   clean      one thread per (head, chunk, slot): keeps an id when it names
 //              a block of the document that starts at or before the chunk's
 //              last query and no earlier slot holds it; counts kept ids per
@@ -43,9 +43,10 @@ __device__ __forceinline__ int block_inclusive_scan(int x, int* s_warp, int* tot
 constexpr int kZeroPerBlock = 16 * kThreads;   // counters cleared per extra workgroup
 
 __global__ __launch_bounds__(kThreads) void geometry_kernel(
-    const int32_t* __restrict__ cu, int num_docs, int T, int C, int R, int B, int max_doc_chunks,
-    int32_t* __restrict__ doc_chunk_off, int32_t* __restrict__ doc_blk_off, int32_t* __restrict__ desc,
-    int32_t* __restrict__ err, int32_t* __restrict__ row_cursor, int64_t n_cursor) {
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ kv_starts, int num_docs, int T, int W, int C,
+    int R, int B, int max_doc_chunks, int32_t* __restrict__ doc_chunk_off, int32_t* __restrict__ doc_blk_off,
+    int32_t* __restrict__ doc_kv_off, int32_t* __restrict__ desc, int32_t* __restrict__ err,
+    int32_t* __restrict__ row_cursor, int64_t n_cursor) {
   __shared__ int s_warp[kThreads / 64];
   const int tid = threadIdx.x;
   if (blockIdx.x > 0) {
@@ -68,6 +69,12 @@ __global__ __launch_bounds__(kThreads) void geometry_kernel(
       nc = (len + kChunk - 1) / kChunk;
       nb = (len + B - 1) / B;
       if (nc > max_doc_chunks) bad = 1;
+      // K/V rows of the document: its own cu_seqlens rows, or its start in a
+      // workspace, in document order without overlap, inside the W rows
+      const int kv0 = kv_starts ? kv_starts[d] : a;
+      const int kv_end = d + 1 < num_docs ? (kv_starts ? kv_starts[d + 1] : e) : W;
+      if (kv0 < 0 || (int64_t)kv0 + len > kv_end) bad = 1;
+      doc_kv_off[d] = kv0;
     }
     int tc, tb;
     const int ic = block_inclusive_scan(nc, s_warp, &tc);
@@ -262,17 +269,18 @@ __global__ __launch_bounds__(kThreads) void sort_kernel(
 }  // namespace
 
 hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const int32_t* sel,
-                                 int32_t* sched, const msa_schedule_layout& L, hipStream_t stream) {
+                                 const int32_t* kv_starts, int32_t* sched, const msa_schedule_layout& L,
+                                 hipStream_t stream) {
   const int Hkv = p.num_kv_heads, C = p.num_chunks, K = p.topk, R = p.num_kblocks;
   const int64_t cap = (int64_t)Hkv * C * K;
   // clean and fill must use the same grid: a slot's counter copy is its
   // workgroup id modulo kCounterCopies in both
   const int64_t n_cursor = (int64_t)kCounterCopies * Hkv * R;
   const unsigned zero_blocks = (unsigned)((n_cursor + kZeroPerBlock - 1) / kZeroPerBlock);
-  hipLaunchKernelGGL(geometry_kernel, dim3(1 + zero_blocks), dim3(kThreads), 0, stream, cu, p.num_docs,
-                     p.total_tokens, C, R, p.block_size, p.max_doc_chunks, sched + L.doc_chunk_off,
-                     sched + L.doc_blk_off, sched + L.desc, sched + L.err, sched + L.row_cursor,
-                     n_cursor);
+  hipLaunchKernelGGL(geometry_kernel, dim3(1 + zero_blocks), dim3(kThreads), 0, stream, cu, kv_starts,
+                     p.num_docs, p.total_tokens, (int)kv_rows_of(p), C, R, p.block_size, p.max_doc_chunks,
+                     sched + L.doc_chunk_off, sched + L.doc_blk_off, sched + L.doc_kv_off, sched + L.desc,
+                     sched + L.err, sched + L.row_cursor, n_cursor);
   const unsigned grid = (unsigned)((cap + kThreads - 1) / kThreads);
   if (cap > 0)
     hipLaunchKernelGGL(clean_kernel, dim3(grid), dim3(kThreads), 0, stream, cu, sel, Hkv, C, K, R, p.block_size,

@@ -17,7 +17,7 @@
  *  - Pointers named "device" must be device pointers, 16-byte aligned.
  *  - Layouts are THD, token-major and contiguous:
  *      q, out, dout, dq : bf16 [T, Hq, D]      (Hq = 16 * Hkv)
- *      k, v, dk, dv     : bf16 [T, Hkv, D]
+ *      k, v, dk, dv     : bf16 [W, Hkv, D]      (W = T unless kv_rows says otherwise)
  *      lse              : fp32 [T, Hq]          (natural log)
  *      cu_seqlens       : int32 [num_docs + 1]  (device; cu[0] = 0, non-decreasing)
  *      sel              : int32 [Hkv, C, topk]  (device; document-local key-block
@@ -59,7 +59,8 @@ typedef struct msa_problem {
   int32_t num_kv_heads;    /* Hkv: index heads == KV heads (one index head per KV head) */
   int32_t q_per_kv;        /* query heads per KV head; must be 16 (8 queries x 16 heads = 128-row tile) */
   int32_t head_dim;        /* D: 64 or 128 */
-  int32_t block_size;      /* B: key block size; must be 64 */
+  int32_t block_size;      /* B: key block size, 64 or 128 (at 128: topk <= 32 and
+                              dq_mode MSA_DQ_DS_BUFFER) */
   int32_t query_chunk;     /* must be 8 (msa_schedule: QUERY_CHUNK) */
   int32_t topk;            /* slots per (index head, chunk); 1..64 */
   int32_t num_chunks;      /* C = sum_d ceil(len_d / 8) */
@@ -69,6 +70,9 @@ typedef struct msa_problem {
   float softmax_scale;     /* usually head_dim ** -0.5 (msa_schedule: SOFTMAX_SCALE) */
   int32_t dq_mode;         /* MSA_DQ_DS_BUFFER, MSA_DQ_RECOMPUTE, MSA_DQ_ATOMIC_POOL or
                               MSA_DQ_ATOMIC_POOL_BF16 */
+  int32_t kv_rows;         /* rows W of k, v, dk, dv: 0 means total_tokens (compact THD: a
+                              document's keys sit at its cu_seqlens rows); with per-document K/V
+                              starts (msa_build_schedule_kv) any W >= total_tokens */
 } msa_problem;
 
 /* How the backward forms dQ.
@@ -107,6 +111,7 @@ typedef struct msa_problem {
  *                 tail_walks, grid_walks, capacity (Hkv*C*topk), 0
  *   err[8]      : [0] dropped selection slots, [1] geometry mismatch flag
  *   doc_chunk_off[num_docs+1], doc_blk_off[num_docs+1] : per-document offsets
+ *   doc_kv_off[num_docs]  : first row of each document in k, v, dk, dv
  *   chunk_doc[C]          : document of each global chunk
  *   sel_clean[Hkv*C*topk] : kept ids in their slots, -1 elsewhere
  *   row_cursor[8*Hkv*R]   : build scratch (8 striped copies of the row counters)
@@ -118,7 +123,7 @@ typedef struct msa_problem {
  *                           order: (index_head, row_linear, q_begin, q_count,
  *                           document_ordinal, document_local_kblock); -1 padding */
 typedef struct msa_schedule_layout {
-  int64_t desc, err, doc_chunk_off, doc_blk_off, chunk_doc, sel_clean, row_cursor,
+  int64_t desc, err, doc_chunk_off, doc_blk_off, doc_kv_off, chunk_doc, sel_clean, row_cursor,
       row_ptr, head_off, q_idx, task_meta, total;
 } msa_schedule_layout;
 
@@ -141,6 +146,24 @@ int msa_schedule_layout_of(const msa_problem* p, msa_schedule_layout* out);
  * (device, msa_schedule_layout_of(...).total int32 elements). */
 int msa_build_schedule(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
                        int32_t* sched, void* stream);
+
+/* msa_build_schedule for K/V held in a workspace with a start row per
+ * document (msa_schedule page: MSABackwardSchedule.document_workspace_starts,
+ * the 128-aligned workspace row of each document; msa_backward_sm100 page:
+ * run_backward takes k_aligned, v_aligned [W, 4, 128] and returns dk, dv in
+ * the same rows, zero outside the documents).  kv_starts (device int32
+ * [num_docs]) gives the row of k / v that holds each document's first key;
+ * documents must lie in order without overlap inside the problem's kv_rows
+ * rows (kv_starts[d] + len_d <= kv_starts[d+1], last one <= kv_rows), else
+ * the schedule's MSA_SCHED_ERR_GEOMETRY word is set and the later kernels
+ * leave their outputs untouched.  Every later call then reads k, v and
+ * writes dk, dv ([kv_rows, Hkv, D]) at those rows; dk and dv rows that hold
+ * no attended key, including every row between documents, are exactly 0.
+ * kv_starts = NULL gives the compact layout (kv_starts[d] = cu_seqlens[d]),
+ * which is what msa_build_schedule does.  Starts need not be multiples of
+ * 128; the pages' aligned workspace is one valid placement. */
+int msa_build_schedule_kv(const msa_problem* p, const int32_t* cu_seqlens, const int32_t* sel,
+                          const int32_t* kv_starts, int32_t* sched, void* stream);
 
 /* Sparse forward (msa_bindings: the flat forward sparse_atten_func; its
  * outputs are the out/lse that run_backward consumes).  For every

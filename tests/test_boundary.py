@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from block_sparse_attention_k2q_amd import binding as B
@@ -133,3 +134,17 @@ def test_tensors_on_different_devices_are_refused():
     import torch
     with pytest.raises(ValueError):
         B._on_device(torch.zeros(1), torch.zeros(1, device="meta"))
+
+
+def test_kv_rows_fewer_than_tokens_is_a_shape_error():
+    p = B.Problem.make(np.array([0, 100, 300], dtype=np.int32), 1, 64, 2)
+    B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "kv_rows": 300}))
+    B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "kv_rows": 4096}))
+    with pytest.raises(ValueError):
+        B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "kv_rows": 299}))
+    with pytest.raises(ValueError):
+        B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "kv_rows": -1}))
+    # the backward scratch grows with the K/V rows (fp32 dK / dV accumulators)
+    grow = (B.msa_backward_scratch_bytes(B.Problem(**{**p.__dict__, "kv_rows": 4096}))
+            - B.msa_backward_scratch_bytes(p))
+    assert grow >= 2 * 4 * (4096 - 300) * 64
