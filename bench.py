@@ -135,6 +135,9 @@ def main() -> int:
     ap.add_argument("--workload", choices=("single8k", "varlen8", "long64k", "zipf16k"), default="single8k",
                     help="single8k is the headline workload; the others are the remaining full-size "
                          "configurations (packed varlen, 64k context at top-32, Zipf-skewed selection)")
+    ap.add_argument("--forward", choices=("query", "kv"), default="query",
+                    help="query: the query-parallel forward (default); kv: the planner-driven forward that "
+                         "walks the task table (KV-parallel, exact cross-workgroup softmax merge)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, run a plain device-to-device copy of this many MiB "
                          "three times (the known-size reference for HBM byte counters)")
@@ -172,6 +175,14 @@ def main() -> int:
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if args.forward == "kv":
+        fwd_scratch = torch.empty(B.msa_forward_kv_scratch_bytes(p), dtype=torch.uint8, device=dev)
+
+        def run_forward():
+            B.msa_forward_kv(p, q, k, v, cu, sched, fwd_scratch, out, lse)
+    else:
+        def run_forward():
+            B.msa_forward(p, q, k, v, cu, sched, out, lse)
 
     names = ("schedule", "forward", "bwd_pre", "bwd_main", "bwd_dq", "bwd_post")
 
@@ -182,7 +193,7 @@ def main() -> int:
         mark(0)
         B.msa_build_schedule(p, cu, sel, sched)
         mark(1)
-        B.msa_forward(p, q, k, v, cu, sched, out, lse)
+        run_forward()
         mark(2)
         B.msa_backward_preprocess(p, out, do, scratch)
         mark(3)
@@ -300,7 +311,8 @@ def main() -> int:
         "config": {"workload": f"{args.workload}: {len(w.cu_seqlens) - 1} document(s), T={w.total_tokens}, "
                                f"{w.num_kv_heads} KV heads x 16 query heads, D={w.head_dim}, "
                                f"key block {args.block}, chunk 8, top-k {w.topk}",
-                   "selected_pairs": n_pairs, "num_cus": num_cus, "dq_mode": args.dq_mode},
+                   "selected_pairs": n_pairs, "num_cus": num_cus, "dq_mode": args.dq_mode,
+                   "forward": args.forward},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernels_ms": {n: round(x, 4) for n, x in per_kernel.items()},
         "kernels_ms_median": {n: round(x, 4) for n, x in per_kernel_median.items()},

@@ -37,6 +37,7 @@ EXPORTED = (
     "msa_backward_scratch_bytes", "msa_backward", "msa_backward_preprocess", "msa_backward_main",
     "msa_backward_dq", "msa_backward_postprocess", "msa_grid_launch_bound", "msa_status_string",
     "msa_index_scratch_bytes", "msa_index_select", "msa_backward_noalloc", "msa_build_schedule_kv",
+    "msa_forward_kv_scratch_bytes", "msa_forward_kv",
 )
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "msa_build_schedule": ([P, i32p, i32p, i32p, vp], ctypes.c_int),
             "msa_build_schedule_kv": ([P, i32p, i32p, i32p, i32p, vp], ctypes.c_int),
             "msa_forward": ([P, vp, vp, vp, i32p, i32p, vp, vp, vp], ctypes.c_int),
+            "msa_forward_kv_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+            "msa_forward_kv": ([P, vp, vp, vp, i32p, i32p, vp, vp, vp, vp], ctypes.c_int),
             "msa_backward_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
             "msa_backward": ([P, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp, vp, vp], ctypes.c_int),
             "msa_backward_preprocess": ([P, vp, vp, vp, vp], ctypes.c_int),
@@ -263,6 +266,38 @@ def msa_forward(p: Problem, q, k, v, cu_seqlens, sched, out, lse, stream=None) -
         ps = p.c_struct()
         _check(lib().msa_forward(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(sched),
                                  _ptr(out), _ptr(lse), _stream(stream)), "msa_forward")
+
+
+def msa_forward_kv_scratch_bytes(p: Problem) -> int:
+    ps = p.c_struct()
+    out = ctypes.c_size_t(0)
+    _check(lib().msa_forward_kv_scratch_bytes(ctypes.byref(ps), ctypes.byref(out)), "msa_forward_kv_scratch_bytes")
+    return int(out.value)
+
+
+def msa_forward_kv(p: Problem, q, k, v, cu_seqlens, sched, scratch, out, lse, stream=None) -> None:
+    """Planner-driven forward (KV-parallel over the task table): same out / lse as msa_forward."""
+    T, hq, hkv, D, W = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim, p.kv_total
+    for name, t, shape in (("q", q, (T, hq, D)), ("k", k, (W, hkv, D)), ("v", v, (W, hkv, D)),
+                           ("out", out, (T, hq, D))):
+        _expect(t, name, torch.bfloat16, shape)
+    _expect(lse, "lse", torch.float32, (T, hq))
+    _expect(cu_seqlens, "cu_seqlens", torch.int32, (p.num_docs + 1,))
+    _expect(sched, "sched", torch.int32, (msa_schedule_layout_of(p).total,))
+    _expect(scratch, "scratch", torch.uint8, (msa_forward_kv_scratch_bytes(p),))
+    with _on_device(q, k, v, cu_seqlens, sched, scratch, out, lse):
+        ps = p.c_struct()
+        _check(lib().msa_forward_kv(ctypes.byref(ps), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), _ptr(sched),
+                                    _ptr(scratch), _ptr(out), _ptr(lse), _stream(stream)), "msa_forward_kv")
+
+
+def forward_kv(p: Problem, q, k, v, cu_seqlens, sched, scratch=None, stream=None):
+    if scratch is None:
+        scratch = torch.empty(msa_forward_kv_scratch_bytes(p), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    msa_forward_kv(p, q, k, v, cu_seqlens, sched, scratch, out, lse, stream)
+    return out, lse
 
 
 def msa_index_scratch_bytes(p: Problem) -> int:

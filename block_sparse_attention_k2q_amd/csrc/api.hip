@@ -109,6 +109,31 @@ int msa_forward(const msa_problem* p, const void* q, const void* k, const void* 
       msa::launch_forward(*p, q, k, v, cu_seqlens, sched, L, out, lse, (hipStream_t)stream));
 }
 
+int msa_forward_kv_scratch_bytes(const msa_problem* p, size_t* bytes) {
+  const int st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->block_size != 64) return MSA_ERR_UNSUPPORTED;
+  if (!bytes) return MSA_ERR_INVALID;
+  *bytes = msa::forward_kv_scratch_layout(*p).total;
+  return MSA_OK;
+}
+
+int msa_forward_kv(const msa_problem* p, const void* q, const void* k, const void* v,
+                   const int32_t* cu_seqlens, const int32_t* sched, void* scratch, void* out, float* lse,
+                   void* stream) {
+  const int st = check_problem(p);
+  if (st != MSA_OK) return st;
+  if (p->block_size != 64) return MSA_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !sched || (p->total_tokens > 0 && (!q || !k || !v || !out || !lse || !scratch)))
+    return MSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(sched) ||
+      !aligned16(scratch) || !aligned16(lse))
+    return MSA_ERR_ALIGN;
+  const msa_schedule_layout L = msa::schedule_layout(*p);
+  return hip_status(
+      msa::launch_forward_kv(*p, q, k, v, cu_seqlens, sched, L, scratch, out, lse, (hipStream_t)stream));
+}
+
 int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes) {
   const int st = check_problem(p);
   if (st != MSA_OK) return st;

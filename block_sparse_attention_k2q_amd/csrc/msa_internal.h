@@ -82,6 +82,22 @@ inline BackwardScratch backward_scratch_layout(const msa_problem& p) {
   return s;
 }
 
+// Scratch of the planner-driven forward (bytes, 256-aligned): per selection
+// slot and query row (m, l) as float2 [Hkv, C, topk, 128], and the fp32
+// output pool [T, Hq, D].
+struct ForwardKvScratch {
+  size_t stats, pool, total;
+};
+inline ForwardKvScratch forward_kv_scratch_layout(const msa_problem& p) {
+  auto a256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+  ForwardKvScratch s;
+  size_t o = 0;
+  s.stats = o; o = a256(o + 8 * (size_t)p.num_kv_heads * p.num_chunks * p.topk * 128);
+  s.pool = o; o = a256(o + 4 * (size_t)p.total_tokens * p.num_kv_heads * p.q_per_kv * p.head_dim);
+  s.total = o;
+  return s;
+}
+
 // Index scorer (scorer.hip): index dimension and the most earlier blocks a
 // chunk can choose from (one LDS score per candidate per wave).
 constexpr int kIndexDim = MSA_INDEX_DIM;
@@ -113,6 +129,9 @@ hipError_t launch_build_schedule(const msa_problem& p, const int32_t* cu, const 
 hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, const void* v,
                           const int32_t* cu, const int32_t* sched, const msa_schedule_layout& L,
                           void* out, float* lse, hipStream_t stream);
+hipError_t launch_forward_kv(const msa_problem& p, const void* q, const void* k, const void* v,
+                             const int32_t* cu, const int32_t* sched, const msa_schedule_layout& L,
+                             void* scratch, void* out, float* lse, hipStream_t stream);
 hipError_t launch_backward_preprocess(const msa_problem& p, const void* out, const void* dout,
                                       void* scratch, hipStream_t stream);
 hipError_t launch_backward_main(const msa_problem& p, const void* q, const void* k, const void* v,

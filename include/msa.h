@@ -175,6 +175,25 @@ int msa_forward(const msa_problem* p, const void* q, const void* k, const void* 
                 const int32_t* cu_seqlens, const int32_t* sched, void* out, float* lse,
                 void* stream);
 
+/* Planner-driven (KV-parallel) forward: the same out and lse as msa_forward,
+ * computed by walking the schedule's task table (one work item per k2q CSR
+ * entry, msa_schedule page: scheduler_metadata; msa_bindings page: the
+ * planner fmha_sm100_plan beside the flat forward) the way the backward does,
+ * key block resident per bucket.  A chunk's blocks then sit in different
+ * workgroups, so the softmax is reduced across them exactly: a statistics
+ * pass (per slot and query row, the block's max and exp-sum), a merge into
+ * the LSE, an output pass with the final probabilities whose O is added into
+ * an fp32 pool with atomics, and a cast.  Slower than msa_forward on MI355X
+ * (two passes over S, one fp32 atomic per output element per block); key
+ * block 64 only (MSA_ERR_UNSUPPORTED otherwise).
+ *   scratch : msa_forward_kv_scratch_bytes bytes (device, 16-byte aligned):
+ *             float2 [Hkv, C, topk, 128] statistics and the fp32 pool
+ *             [T, Hq, D] (8K tokens x 64 heads x 128: 256 MiB + 64 MiB). */
+int msa_forward_kv_scratch_bytes(const msa_problem* p, size_t* bytes);
+int msa_forward_kv(const msa_problem* p, const void* q, const void* k, const void* v,
+                   const int32_t* cu_seqlens, const int32_t* sched, void* scratch, void* out,
+                   float* lse, void* stream);
+
 /* Bytes of scratch msa_backward needs: fp32 Delta [T, Hq], fp32 dK and dV
  * accumulators [T, Hkv, D]; in MSA_DQ_ATOMIC_POOL mode the fp32 dQ pool
  * [T, Hq, D]; in MSA_DQ_DS_BUFFER mode the bf16 dS slots
