@@ -201,7 +201,7 @@ def main() -> int:
         mark(4)
         B.msa_backward_dq(p, q, k, v, do, lse, cu, sched, scratch, dq)
         mark(5)
-        B.msa_backward_postprocess(p, scratch, dq, dk, dv)
+        B.msa_backward_postprocess(p, sched, scratch, dq, dk, dv)
         mark(6)
 
     def event_rows(n):

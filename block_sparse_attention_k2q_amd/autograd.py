@@ -42,14 +42,23 @@ def msa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens:
                   dq_mode: int = B.DQ_DS_BUFFER, return_lse: bool = False):
     """Sparse attention over THD tensors: q [T, 16*Hkv, D], k / v [T, Hkv, D]
     (bf16, on one GPU), cu_seqlens int32 [docs + 1], sel int32 [Hkv, C, topk]
-    of document-local key-block ids (-1 = empty slot).  Without `problem`,
-    the sizes are derived from the shapes and a host copy of cu_seqlens."""
+    of document-local key-block ids (-1 = empty slot).
+
+    The host-side sizes (the Problem) come from `problem` when given; else
+    from cu_seqlens: on the host (a CPU tensor or an array) it is read there
+    and copied to the device, on the device it is copied to the host first,
+    which waits for the device.  Pass `problem` (built once from the host
+    lengths) or host cu_seqlens to keep the call free of that wait."""
+    dev = q.device
     if problem is None:
         if q.dim() != 3 or k.dim() != 3 or sel.dim() != 3:
             raise ValueError("q, k must be [T, H, D] and sel [Hkv, C, topk]")
-        cu_host = cu_seqlens.detach().to("cpu").numpy()
+        on_device = isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda
+        cu_host = (cu_seqlens.detach().to("cpu") if on_device else torch.as_tensor(cu_seqlens)).numpy()
         problem = B.Problem.make(cu_host, k.shape[1], q.shape[2], sel.shape[2],
-                                 num_cus=B.msa_device_check(q.device.index or 0),
+                                 num_cus=B.msa_device_check(dev.index or 0),
                                  softmax_scale=softmax_scale, block_size=block_size, dq_mode=dq_mode)
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda):
+        cu_seqlens = torch.as_tensor(cu_seqlens, dtype=torch.int32).to(dev)
     out, lse = MSAAttentionFunction.apply(q, k, v, cu_seqlens, sel, problem)
     return (out, lse) if return_lse else out

@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
             "msa_backward_preprocess": ([P, vp, vp, vp, vp], ctypes.c_int),
             "msa_backward_main": ([P, vp, vp, vp, vp, vp, i32p, i32p, vp, vp], ctypes.c_int),
             "msa_backward_dq": ([P, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp], ctypes.c_int),
-            "msa_backward_postprocess": ([P, vp, vp, vp, vp, vp], ctypes.c_int),
+            "msa_backward_postprocess": ([P, i32p, vp, vp, vp, vp, vp], ctypes.c_int),
             "msa_grid_launch_bound": ([ctypes.c_int64, ctypes.c_int32], ctypes.c_int64),
             "msa_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "msa_index_scratch_bytes": ([P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
@@ -410,16 +410,16 @@ def msa_backward_dq(p: Problem, q, k, v, dout, lse, cu_seqlens, sched, scratch, 
                "msa_backward_dq")
 
 
-def msa_backward_postprocess(p: Problem, scratch, dq, dk, dv, stream=None) -> None:
-    _check_bwd_inputs(p, None, None, None, None, None, None, None, None, scratch)
+def msa_backward_postprocess(p: Problem, sched, scratch, dq, dk, dv, stream=None) -> None:
+    _check_bwd_inputs(p, None, None, None, None, None, None, None, sched, scratch)
     T, hq, hkv, D = p.total_tokens, p.num_q_heads, p.num_kv_heads, p.head_dim
     _expect(dq, "dq", torch.bfloat16, (T, hq, D))
     _expect(dk, "dk", torch.bfloat16, (p.kv_total, hkv, D))
     _expect(dv, "dv", torch.bfloat16, (p.kv_total, hkv, D))
-    with _on_device(scratch, dq, dk, dv):
+    with _on_device(sched, scratch, dq, dk, dv):
         ps = p.c_struct()
-        _check(lib().msa_backward_postprocess(ctypes.byref(ps), _ptr(scratch), _ptr(dq), _ptr(dk), _ptr(dv),
-                                              _stream(stream)), "msa_backward_postprocess")
+        _check(lib().msa_backward_postprocess(ctypes.byref(ps), _ptr(sched), _ptr(scratch), _ptr(dq), _ptr(dk),
+                                              _ptr(dv), _stream(stream)), "msa_backward_postprocess")
 
 
 def msa_grid_launch_bound(capacity: int, num_cus: int) -> int:

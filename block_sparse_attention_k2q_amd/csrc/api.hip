@@ -182,13 +182,15 @@ int msa_backward_dq(const msa_problem* p, const void* q, const void* k, const vo
                                             (hipStream_t)stream));
 }
 
-int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk, void* dv,
-                             void* stream) {
+int msa_backward_postprocess(const msa_problem* p, const int32_t* sched, const void* scratch, void* dq,
+                             void* dk, void* dv, void* stream) {
   const int st = check_problem(p);
   if (st != MSA_OK) return st;
-  if (p->total_tokens > 0 && (!scratch || !dq || !dk || !dv)) return MSA_ERR_INVALID;
-  if (!aligned16(scratch) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return MSA_ERR_ALIGN;
-  return hip_status(msa::launch_backward_postprocess(*p, scratch, dq, dk, dv, (hipStream_t)stream));
+  if (!sched || (p->total_tokens > 0 && (!scratch || !dq || !dk || !dv))) return MSA_ERR_INVALID;
+  if (!aligned16(scratch) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(sched))
+    return MSA_ERR_ALIGN;
+  const msa_schedule_layout L = msa::schedule_layout(*p);
+  return hip_status(msa::launch_backward_postprocess(*p, sched, L, scratch, dq, dk, dv, (hipStream_t)stream));
 }
 
 int msa_backward(const msa_problem* p, const void* q, const void* k, const void* v, const void* out,
@@ -200,7 +202,7 @@ int msa_backward(const msa_problem* p, const void* q, const void* k, const void*
   if (st != MSA_OK) return st;
   st = msa_backward_dq(p, q, k, v, dout, lse, cu_seqlens, sched, scratch, dq, stream);
   if (st != MSA_OK) return st;
-  return msa_backward_postprocess(p, scratch, dq, dk, dv, stream);
+  return msa_backward_postprocess(p, sched, scratch, dq, dk, dv, stream);
 }
 
 static int check_index_problem(const msa_problem* p) {

@@ -79,7 +79,14 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
                                                           const float* __restrict__ dv_acc,
                                                           bf16* __restrict__ dq, bf16* __restrict__ dk,
                                                           bf16* __restrict__ dv, int64_t n_q_vec,
-                                                          int64_t n_kv_vec, float scale) {
+                                                          int64_t n_kv_vec, float scale,
+                                                          const int32_t* __restrict__ err) {
+  if (err[1]) {   // geometry mismatch: the main kernel did not run
+    fill_nan(dq, n_q_vec, nullptr, 0);
+    fill_nan(dk, n_kv_vec, nullptr, 0);
+    fill_nan(dv, n_kv_vec, nullptr, 0);
+    return;
+  }
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   auto cast8 = [](const float* src, bf16* dst, float mul) {
     const floatx4 a = reinterpret_cast<const floatx4*>(src)[0];
@@ -103,7 +110,12 @@ __global__ __launch_bounds__(256) void postprocess_kernel(const float* __restric
 // writes dq elements 8x .. 8x+7 = (token, head h, d0 .. d0+7).
 template <int D>
 __global__ __launch_bounds__(256) void pool_bf16_to_dq_kernel(const bf16* __restrict__ pool,
-                                                              bf16* __restrict__ dq, int64_t n_q_vec) {
+                                                              bf16* __restrict__ dq, int64_t n_q_vec,
+                                                              const int32_t* __restrict__ err) {
+  if (err[1]) {
+    fill_nan(dq, n_q_vec, nullptr, 0);
+    return;
+  }
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= n_q_vec) return;
   const int64_t e = 8 * x;
@@ -893,7 +905,8 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
   return go_kv(backward_kv_kernel<64, false, 1>, 1);
 }
 
-hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
+hipError_t launch_backward_postprocess(const msa_problem& p, const int32_t* sched,
+                                       const msa_schedule_layout& S, const void* scratch, void* dq, void* dk,
                                        void* dv, hipStream_t stream) {
   const BackwardScratch L = backward_scratch_layout(p);
   const uint8_t* base = (const uint8_t*)scratch;
@@ -906,13 +919,13 @@ hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch
   hipLaunchKernelGGL(postprocess_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
                      (const float*)(base + L.dq_pool), (const float*)(base + L.dk_acc),
                      (const float*)(base + L.dv_acc), (bf16*)dq, (bf16*)dk, (bf16*)dv, n_q_vec, n_kv_vec,
-                     p.softmax_scale);
+                     p.softmax_scale, sched + S.err);
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL_BF16) {
     const int64_t n_pool_vec = (int64_t)p.total_tokens * hq * p.head_dim / 8;
     if (n_pool_vec > 0) {
       auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3((unsigned)((n_pool_vec + 255) / 256)), dim3(256), 0, stream,
-                           (const bf16*)(base + L.dq_pool), (bf16*)dq, n_pool_vec);
+                           (const bf16*)(base + L.dq_pool), (bf16*)dq, n_pool_vec, sched + S.err);
       };
       if (p.head_dim == 128) go(pool_bf16_to_dq_kernel<128>);
       else go(pool_bf16_to_dq_kernel<64>);

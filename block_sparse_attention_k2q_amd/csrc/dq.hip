@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
     const int32_t* __restrict__ chunk_doc, const int32_t* __restrict__ doc_chunk_off,
     const int32_t* __restrict__ doc_kv_off, const int32_t* __restrict__ sel_clean,
     const int32_t* __restrict__ err, bf16* __restrict__ dq,
-    int Hkv, int C, int K, int sub, float scale) {
+    int Hkv, int C, int K, int sub, float scale, int T) {
   constexpr int CPR = D / 8;
   constexpr int NT = D / 32;
   constexpr int NW = kDqThreads / 64;
@@ -46,7 +46,10 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_from_ds_kernel(
   __shared__ int s_block[64];
   __shared__ int s_n;
 
-  if (err[1]) return;
+  if (err[1]) {
+    fill_nan(dq, (int64_t)T * Hkv * kQPerKV * D / 8, nullptr, 0);
+    return;
+  }
   const int i = blockIdx.x % Hkv;
   const int g = blockIdx.x / Hkv;
   const int d = chunk_doc[g];
@@ -149,8 +152,8 @@ hipError_t launch_backward_dq(const msa_problem& p, const void* q, const void* k
       hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)k,
                          (const bf16*)((const uint8_t*)scratch + S.ds), cu, sched + L.chunk_doc,
                          sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean, sched + L.err,
-                         (bf16*)dq,
-                         p.num_kv_heads, p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
+                         (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.block_size / kBlock,
+                         p.softmax_scale, p.total_tokens);
     };
     if (p.head_dim == 128) go_ds(dq_from_ds_kernel<128>);
     else go_ds(dq_from_ds_kernel<64>);

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_kv_off,
     const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv,
-    int C, int K, float scale) {
+    int C, int K, float scale, int T) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
@@ -45,7 +45,10 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
   __shared__ int s_blocks[64];
   __shared__ int s_nblocks;
 
-  if (err[1]) return;
+  if (err[1]) {
+    fill_nan(dq, (int64_t)T * Hkv * kQPerKV * D / 8, nullptr, 0);
+    return;
+  }
   const int i = blockIdx.x % Hkv;
   const int g = blockIdx.x / Hkv;
   const int d = chunk_doc[g];
@@ -200,8 +203,8 @@ hipError_t launch_dq_recompute(const msa_problem& p, const void* q, const void* 
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta, cu,
                        sched + L.chunk_doc, sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean,
-                       sched + L.err,
-                       (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale);
+                       sched + L.err, (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale,
+                       p.total_tokens);
   };
   if (p.head_dim == 128) go(dq_kernel<128>);
   else go(dq_kernel<64>);

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_kv_off,
     const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ out,
     float* __restrict__ lse, int Hkv, int C,
-    int K, int sub, float scale) {
+    int K, int sub, float scale, int T) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;           // k steps of S^T = K Q^T
   constexpr int NT = D / 32;           // 32-wide d tiles of O^T
@@ -86,7 +86,10 @@ __global__ __launch_bounds__(kFwdThreads, 2) void forward_kernel(
   __shared__ __attribute__((aligned(16))) bf16 vb0[kBlock * D];
   __shared__ __attribute__((aligned(16))) bf16 vb1[kBlock * D];
 
-  if (err[1]) return;
+  if (err[1]) {
+    fill_nan(out, (int64_t)T * Hkv * kQPerKV * D / 8, lse, (int64_t)T * Hkv * kQPerKV);
+    return;
+  }
   const int i = blockIdx.x % Hkv;
   const int g = blockIdx.x / Hkv;
   const int d = chunk_doc[g];
@@ -350,7 +353,7 @@ hipError_t launch_forward(const msa_problem& p, const void* q, const void* k, co
                        (const bf16*)k, (const bf16*)v, cu, sched + L.chunk_doc, sched + L.doc_chunk_off,
                        sched + L.doc_kv_off, sched + L.sel_clean, sched + L.err, (bf16*)out, lse,
                        p.num_kv_heads,
-                       p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale);
+                       p.num_chunks, p.topk, p.block_size / kBlock, p.softmax_scale, p.total_tokens);
   };
   if (p.head_dim == 128) args(forward_kernel<128>, kFwdThreads);
   else args(forward_kernel<64>, kFwdThreads);

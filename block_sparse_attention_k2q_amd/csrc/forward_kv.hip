@@ -259,7 +259,13 @@ __global__ __launch_bounds__(kTileM) void forward_kv_merge_kernel(
 }
 
 __global__ __launch_bounds__(256) void forward_kv_cast_kernel(const float* __restrict__ pool,
-                                                              bf16* __restrict__ out, int64_t n_vec) {
+                                                              bf16* __restrict__ out, int64_t n_vec,
+                                                              float* __restrict__ lse, int64_t n_lse,
+                                                              const int32_t* __restrict__ err) {
+  if (err[1]) {   // geometry mismatch: the passes before did not run
+    fill_nan(out, n_vec, lse, n_lse);
+    return;
+  }
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (x >= n_vec) return;
   const floatx4 a = reinterpret_cast<const floatx4*>(pool)[2 * x];
@@ -309,7 +315,8 @@ hipError_t launch_forward_kv(const msa_problem& p, const void* q, const void* k,
   const int64_t n_vec = (int64_t)p.total_tokens * p.num_kv_heads * kQPerKV * p.head_dim / 8;
   if (n_vec > 0)
     hipLaunchKernelGGL(forward_kv_cast_kernel, dim3((unsigned)((n_vec + 255) / 256)), dim3(256), 0, stream,
-                       (const float*)pool, (bf16*)out, n_vec);
+                       (const float*)pool, (bf16*)out, n_vec, lse,
+                       (int64_t)p.total_tokens * p.num_kv_heads * kQPerKV, sched + L.err);
   return hipGetLastError();
 }
 

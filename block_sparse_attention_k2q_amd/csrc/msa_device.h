@@ -351,6 +351,19 @@ __device__ int block_inclusive_scan_n(int x, int* s_warp, int* total) {
   return x + add;
 }
 
+// What a kernel writes instead of its outputs when the schedule's geometry
+// check failed (cu_seqlens disagree with the host sizes): NaN in n8 groups of
+// 8 bf16 at p and n1 floats at f, grid-stride over every thread of the
+// launch.  The sizes come from the host, so the fill stays in bounds
+// whatever cu_seqlens hold.
+__device__ __forceinline__ void fill_nan(bf16* p, int64_t n8, float* f, int64_t n1) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const u32x4 nan8 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  for (int64_t x = t; x < n8; x += stride) *reinterpret_cast<u32x4*>(p + 8 * x) = nan8;
+  for (int64_t x = t; x < n1; x += stride) f[x] = __builtin_nanf("");
+}
+
 // Index of the last element <= x in a non-decreasing array a[0..n) (a[0] <= x).
 __device__ __forceinline__ int upper_bound_minus1(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;  // invariant: a[lo] <= x, answer in [lo, hi)

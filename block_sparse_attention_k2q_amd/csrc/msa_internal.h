@@ -146,7 +146,8 @@ hipError_t launch_dq_recompute(const msa_problem& p, const void* q, const void* 
                                const void* dout, const float* lse, const int32_t* cu, const int32_t* sched,
                                const msa_schedule_layout& L, const void* scratch, void* dq,
                                hipStream_t stream);
-hipError_t launch_backward_postprocess(const msa_problem& p, const void* scratch, void* dq, void* dk,
+hipError_t launch_backward_postprocess(const msa_problem& p, const int32_t* sched,
+                                       const msa_schedule_layout& L, const void* scratch, void* dq, void* dk,
                                        void* dv, hipStream_t stream);
 
 }  // namespace msa

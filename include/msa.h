@@ -52,7 +52,10 @@ typedef enum msa_status {
 
 /* Problem geometry; all fields are host integers.  num_chunks, num_kblocks
  * and max_doc_chunks must agree with cu_seqlens (the schedule build checks
- * this on the device and sets MSA_SCHED_ERR_GEOMETRY if they do not). */
+ * this on the device and sets MSA_SCHED_ERR_GEOMETRY if they do not; every
+ * later call on that schedule then writes NaN to all of its outputs --
+ * out, lse, dq, dk, dv -- instead of computing them, so the failure shows
+ * without a host synchronisation; the index scorer writes empty rows). */
 typedef struct msa_problem {
   int32_t total_tokens;    /* T = cu_seqlens[num_docs] */
   int32_t num_docs;        /* >= 1 */
@@ -155,8 +158,8 @@ int msa_build_schedule(const msa_problem* p, const int32_t* cu_seqlens, const in
  * [num_docs]) gives the row of k / v that holds each document's first key;
  * documents must lie in order without overlap inside the problem's kv_rows
  * rows (kv_starts[d] + len_d <= kv_starts[d+1], last one <= kv_rows), else
- * the schedule's MSA_SCHED_ERR_GEOMETRY word is set and the later kernels
- * leave their outputs untouched.  Every later call then reads k, v and
+ * the schedule's MSA_SCHED_ERR_GEOMETRY word is set and the later calls
+ * write NaN to their outputs.  Every later call then reads k, v and
  * writes dk, dv ([kv_rows, Hkv, D]) at those rows; dk and dv rows that hold
  * no attended key, including every row between documents, are exactly 0.
  * kv_starts = NULL gives the compact layout (kv_starts[d] = cu_seqlens[d]),
@@ -243,8 +246,8 @@ int msa_backward_main(const msa_problem* p, const void* q, const void* k, const 
 int msa_backward_dq(const msa_problem* p, const void* q, const void* k, const void* v,
                     const void* dout, const float* lse, const int32_t* cu_seqlens,
                     const int32_t* sched, const void* scratch, void* dq, void* stream);
-int msa_backward_postprocess(const msa_problem* p, const void* scratch, void* dq, void* dk,
-                             void* dv, void* stream);
+int msa_backward_postprocess(const msa_problem* p, const int32_t* sched, const void* scratch,
+                             void* dq, void* dk, void* dv, void* stream);
 
 /* Index scorer and top-k block selection: the step that produces `sel`.
  * msa_bindings: MSAKernels lists the scorer (fmha_sm100) beside the planner;

@@ -17,26 +17,38 @@ import msa_testlib as TL
 pytestmark = pytest.mark.gpu
 
 
-def test_geometry_mismatch_is_flagged_and_outputs_untouched():
+def test_geometry_mismatch_is_flagged_and_outputs_are_nan():
     w = make_workload("tiny", lengths=[512], num_kv_heads=1, head_dim=64, topk=4, seed=41)
     print(f"[case] geometry mismatch T={w.total_tokens}", flush=True)
-    p = TL.problem_for(w, dq_mode=B.DQ_DS_BUFFER)
-    t = TL.to_dev(w)
-    bad_cu = torch.tensor([0, 448], dtype=torch.int32, device=t["cu"].device)   # host says 512
-    sched = B.build_schedule(p, bad_cu, t["sel"])
+    for dq_mode in (B.DQ_DS_BUFFER, B.DQ_RECOMPUTE, B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16):
+        p = TL.problem_for(w, dq_mode=dq_mode)
+        t = TL.to_dev(w)
+        bad_cu = torch.tensor([0, 448], dtype=torch.int32, device=t["cu"].device)   # host says 512
+        sched = B.build_schedule(p, bad_cu, t["sel"])
+        torch.cuda.synchronize()
+        views = TL.schedule_host(p, sched)
+        assert views["err"][B.SCHED_ERR_GEOMETRY] == 1
+        assert np.all(views["sel_clean"] == -1)
+        # the step-by-step calls and the high-level ones: every output NaN
+        out = torch.full_like(t["q"], 7.0)
+        lse = torch.full((w.total_tokens, w.num_q_heads), 7.0, dtype=torch.float32, device=out.device)
+        B.msa_forward(p, t["q"], t["k"], t["v"], bad_cu, sched, out, lse)
+        scratch = B.alloc_scratch(p, out.device)
+        dq, dk, dv = (torch.full_like(x, 7.0) for x in (t["q"], t["k"], t["v"]))
+        B.msa_backward(p, t["q"], t["k"], t["v"], out, t["do"], lse, bad_cu, sched, scratch, dq, dk, dv)
+        o2, l2 = B.forward(p, t["q"], t["k"], t["v"], bad_cu, sched)
+        g2 = B.backward(p, t["q"], t["k"], t["v"], o2, t["do"], l2, bad_cu, sched)
+        o3, l3 = B.forward_kv(p, t["q"], t["k"], t["v"], bad_cu, sched)
+        torch.cuda.synchronize()
+        for x in (out, lse, dq, dk, dv, o2, l2, *g2, o3, l3):
+            assert torch.isnan(x).all()
+    # the autograd entry point with a problem that disagrees with cu_seqlens
+    from block_sparse_attention_k2q_amd.autograd import msa_attention
+    qg = t["q"].clone().requires_grad_(True)
+    o4 = msa_attention(qg, t["k"], t["v"], bad_cu, t["sel"], problem=p)
+    o4.float().sum().backward()
     torch.cuda.synchronize()
-    views = TL.schedule_host(p, sched)
-    assert views["err"][B.SCHED_ERR_GEOMETRY] == 1
-    assert np.all(views["sel_clean"] == -1)
-    out = torch.full_like(t["q"], 7.0)
-    lse = torch.full((w.total_tokens, w.num_q_heads), 7.0, dtype=torch.float32, device=out.device)
-    B.msa_forward(p, t["q"], t["k"], t["v"], bad_cu, sched, out, lse)
-    scratch = B.alloc_scratch(p, out.device)
-    dq, dk, dv = (torch.full_like(x, 7.0) for x in (t["q"], t["k"], t["v"]))
-    B.msa_backward_main(p, t["q"], t["k"], t["v"], t["do"], lse, bad_cu, sched, scratch)
-    B.msa_backward_dq(p, t["q"], t["k"], t["v"], t["do"], lse, bad_cu, sched, scratch, dq)
-    torch.cuda.synchronize()
-    assert torch.all(out == 7.0) and torch.all(lse == 7.0) and torch.all(dq == 7.0)
+    assert torch.isnan(o4).all() and torch.isnan(qg.grad).all()
     qi, ki = make_index_inputs(w)
     sel = B.index_select(p, qi.to(out.device), ki.to(out.device), bad_cu)
     torch.cuda.synchronize()
