@@ -198,10 +198,13 @@ int msa_forward_kv(const msa_problem* p, const void* q, const void* k, const voi
                    float* lse, void* stream);
 
 /* Bytes of scratch msa_backward needs: fp32 Delta [T, Hq], fp32 dK and dV
- * accumulators [T, Hkv, D]; in MSA_DQ_ATOMIC_POOL mode the fp32 dQ pool
+ * accumulators [kv_rows, Hkv, D]; in MSA_DQ_ATOMIC_POOL mode the fp32 dQ pool
  * [T, Hq, D]; in MSA_DQ_DS_BUFFER mode the bf16 dS slots
- * [Hkv, C, topk, 128, 64] (16 KiB per slot); in MSA_DQ_ATOMIC_POOL_BF16 mode
- * the bf16 pool [T, Hq/2, D, 2]. */
+ * [Hkv, C, topk, block_size / 64, 128, 64] (16 KiB per selection slot and
+ * 64-key tile); in MSA_DQ_ATOMIC_POOL_BF16 mode the bf16 pool [T, Hq/2, D, 2].
+ * With 4 x 16 heads and head dim 128, MSA_DQ_DS_BUFFER needs about 1 GiB for
+ * an 8K-token top-16 problem, 16 GiB for a 64K-token top-32 problem and twice
+ * that at key block 128; MSA_DQ_RECOMPUTE needs 34 MiB and 272 MiB. */
 int msa_backward_scratch_bytes(const msa_problem* p, size_t* bytes);
 
 /* KV-parallel backward (msa_backward_sm100: run_backward): preprocess
