@@ -143,8 +143,8 @@ __device__ __forceinline__ bf16x8 lds_tr_operand_swz8b(const bf16* tile, int col
 
 // Direct global -> LDS copy of 16 bytes per lane: lane l of the wave writes
 // bytes [16 l, 16 l + 16) after lds_wave_base (wave-uniform), reading from a
-// wave-uniform base plus the lane's 32-bit byte offset.
-// runs per copy.  The buffer form also keeps the compiler's LDS waits exact:
+// wave-uniform base plus the lane's 32-bit byte offset (the buffer form of
+// the copy).  The buffer form also keeps the compiler's LDS waits exact:
 // the global form is a flat-encoded instruction, and while one is pending
 // the compiler waits for every outstanding LDS read (lgkmcnt(0)) wherever it
 // needs only the oldest.
