@@ -106,8 +106,6 @@ def _replay(w, num_sms=256, kv_starts=None, kv_rows=None):
 @pytest.mark.parametrize("name", ["tiny", "single8k", "varlen8", "long64k", "zipf16k"])
 @pytest.mark.parametrize("block", [64, 128])
 def test_replay_full_size_workloads(name, block):
-    if name == "long64k" and block == 128:
-        pytest.skip("covered by the key-block-64 case; the same arithmetic at half the tasks")
     w = make_workload(name, block=block)
     n = _replay(w)
     assert n > 0
