@@ -43,11 +43,16 @@ KERNEL_NAMES = {  # per dq mode
                   "bwd_dq": "dq_kernel<128>"},
     "ds": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true, 1>",
            "bwd_dq": "dq_from_ds_kernel<128>"},
-    # key block 128: both 64-key tiles of a block in one 8-wave workgroup
-    "ds_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true, 2>",
-                "bwd_dq": "dq_from_ds_kernel<128>"},
     "atomic": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, false>"},
     "atomic_bf16": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
+    # key block 128: the KV-parallel kernel holds both 64-key tiles of a block
+    # in one 8-wave workgroup; the pool kernel takes them on two workgroups
+    "ds_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, true, 2>",
+                "bwd_dq": "dq_from_ds_kernel<128>"},
+    "recompute_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_kv_kernel<128, false, 2>",
+                       "bwd_dq": "dq_kernel<128>"},
+    "atomic_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, false>"},
+    "atomic_bf16_b128": {"forward": "forward_kernel<128>", "bwd_main": "backward_main_kernel<128, true>"},
 }
 
 
@@ -61,7 +66,7 @@ def kernel_source_hash(kernel: str, mode: str = "ds") -> str:
     device header and the compiler flags that file gets."""
     from block_sparse_attention_k2q_amd import build as msa_build
     h = hashlib.sha256()
-    files = KERNEL_FILES_RECOMPUTE if mode == "recompute" else KERNEL_FILES
+    files = KERNEL_FILES_RECOMPUTE if mode.startswith("recompute") else KERNEL_FILES
     for rel in (files[kernel], "msa_device.h"):
         with open(os.path.join(ROOT, "block_sparse_attention_k2q_amd", "csrc", rel), "rb") as f:
             h.update(f.read())
@@ -131,7 +136,7 @@ def main() -> int:
     ap.add_argument("--dq-mode", choices=("ds", "recompute", "atomic", "atomic_bf16"), default="ds")
     ap.add_argument("--block", type=int, choices=(64, 128), default=64,
                     help="key block size: 64 (the headline workload) or 128 (the same workload at the "
-                         "pages' production block size; dq mode ds only)")
+                         "pages' production block size)")
     ap.add_argument("--workload", choices=("single8k", "varlen8", "long64k", "zipf16k"), default="single8k",
                     help="single8k is the headline workload; the others are the remaining full-size "
                          "configurations (packed varlen, 64k context at top-32, Zipf-skewed selection)")
@@ -145,9 +150,6 @@ def main() -> int:
     global WORKLOAD
     WORKLOAD = args.workload
     if args.block == 128:
-        if args.dq_mode != "ds":
-            print("key block 128 runs with --dq-mode ds only", file=sys.stderr)
-            return 2
         WORKLOAD = args.workload + "_b128"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no multi-GPU "
@@ -267,7 +269,7 @@ def main() -> int:
 
     fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
     gemm = bwd_f // 5
-    names_key = "ds_b128" if args.block == 128 else args.dq_mode
+    names_key = args.dq_mode + ("_b128" if args.block == 128 else "")
     value = n_pairs * (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
     # useful contractions per pair done by each kernel
     pool = dq_mode in (B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16)

@@ -32,9 +32,8 @@ int check_problem(const msa_problem* p) {
       p->max_doc_chunks > MSA_MAX_DOC_CHUNKS)
     return MSA_ERR_UNSUPPORTED;
   // Key block 128 runs as two 64-key halves: at most 64 halves per
-  // selection row, and dQ from the stored dS only.
-  if (p->block_size == 128 && (p->topk > 32 || p->dq_mode != MSA_DQ_DS_BUFFER))
-    return MSA_ERR_UNSUPPORTED;
+  // selection row (one per lane of the wave that compacts the row).
+  if (p->block_size == 128 && p->topk > 32) return MSA_ERR_UNSUPPORTED;
   // Size limits so every flat index fits the 32/64-bit arithmetic the kernels use.
   const int64_t cap = (int64_t)p->num_kv_heads * p->num_chunks * p->topk;
   if (cap > (int64_t)INT32_MAX / 6 || (int64_t)p->num_kv_heads * (p->num_kblocks + 1) > INT32_MAX)

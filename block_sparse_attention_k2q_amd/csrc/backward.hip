@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ task_meta,
     const int32_t* __restrict__ desc, const int32_t* __restrict__ err, void* __restrict__ dq_pool,
     float* __restrict__ dk_acc, float* __restrict__ dv_acc, const int32_t* __restrict__ doc_kv_off, int Hkv,
-    float scale) {
+    int sub, float scale) {
   using S = BwdSmem<D>;
   constexpr int LDK = S::LDK, LDP = S::LDP;
   constexpr int KS = D / 16;                 // k steps over d
@@ -170,7 +170,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
 
   if (err[1]) return;
   const int grid_walks = desc[5];
-  const int wg = blockIdx.x;
+  // Key block 128 (sub = 2): workgroup 2x + kt takes the 64-key half kt of
+  // every task of walk x.
+  const int wg = blockIdx.x / sub;
+  const int kt = blockIdx.x % sub;
   if (wg >= grid_walks) return;
   const int rpc = desc[1], full = desc[2], tail = desc[3], tail_walks = desc[4];
   int lo, hi;
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     int* m = sm.meta[e];
 #pragma unroll
     for (int x = 0; x < 6; ++x) m[x] = tm[x];
+    m[5] = sub * tm[5] + kt;     // the task's 64-key tile
     const int d = tm[4];
     const int t0 = cu[d];
     m[6] = t0;
@@ -269,7 +273,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
     const int tok0 = mrow[6], len = mrow[7], kv0 = mrow[8];
     lds_barrier();  // previous tile fully consumed
     if (i != cur_i || r != cur_r) {
-      if (cur_i >= 0) flush();
+      // a half tile that starts past the document end holds no key
+      if (cur_i >= 0 && cur_b * kBlock < cur_len) flush();
 #pragma unroll
       for (int x = 0; x < OUT_TILES; ++x) {
         acc_dv[x] = floatx16{};
@@ -456,7 +461,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void backward_main_kernel(
       }
     }
   }
-  if (cur_i >= 0) flush();
+  if (cur_i >= 0 && cur_b * kBlock < cur_len) flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -862,15 +867,16 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
   uint8_t* base = (uint8_t*)scratch;
   const int64_t cap = (int64_t)p.num_kv_heads * p.num_chunks * p.topk;
   const int64_t grid = grid_launch_bound(cap, p.num_cus);
+  const int sub = p.block_size / kBlock;
   auto go = [&](auto kern, size_t lds) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), lds, stream, (const bf16*)q,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(sub * grid)), dim3(kBwdThreads), lds, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
                        sched + L.err, (void*)(base + S.dq_pool), (float*)(base + S.dk_acc),
-                       (float*)(base + S.dv_acc), sched + L.doc_kv_off, p.num_kv_heads, p.softmax_scale);
+                       (float*)(base + S.dv_acc), sched + L.doc_kv_off, p.num_kv_heads, sub, p.softmax_scale);
     return hipGetLastError();
   };
   if (p.dq_mode == MSA_DQ_ATOMIC_POOL) {
@@ -884,7 +890,6 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
   // Two workgroups per walk, one per query half of every task tile; with
   // key block 128 each holds both 64-key tiles of the block (8 waves).
   auto go_kv = [&](auto kern, int kt) {
-    const int sub = p.block_size / kBlock;
     hipLaunchKernelGGL(kern, dim3((unsigned)(2 * grid)), dim3(kBwdThreads * kt), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse,
                        (const float*)(base + S.delta), cu, sched + L.task_meta, sched + L.desc,
@@ -893,9 +898,13 @@ hipError_t launch_backward_main(const msa_problem& p, const void* q, const void*
                        p.num_kv_heads, p.num_chunks, p.topk, sub, p.softmax_scale);
     return hipGetLastError();
   };
-  if (p.block_size == 128) {   // dS-buffer mode only (checked at the boundary)
-    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true, 2>, 2);
-    return go_kv(backward_kv_kernel<64, true, 2>, 2);
+  if (p.block_size == 128) {
+    if (p.dq_mode == MSA_DQ_DS_BUFFER) {
+      if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true, 2>, 2);
+      return go_kv(backward_kv_kernel<64, true, 2>, 2);
+    }
+    if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, false, 2>, 2);
+    return go_kv(backward_kv_kernel<64, false, 2>, 2);
   }
   if (p.dq_mode == MSA_DQ_DS_BUFFER) {
     if (p.head_dim == 128) return go_kv(backward_kv_kernel<128, true, 1>, 1);

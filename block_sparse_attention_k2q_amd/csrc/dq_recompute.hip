@@ -12,7 +12,9 @@
 //
 //  * one workgroup per (chunk, index head), 4 waves x 32 query rows; Q and
 //    dO rows of the tile stay in registers as MFMA B operands;
-//  * per kept block: K and V arrive in one of two swizzled LDS buffers by
+//  * per kept 64-key tile (a selected block of 128 keys is two tiles; a tile
+//    whose first key lies after the chunk's last query is dropped): K and V
+//    arrive in one of two swizzled LDS buffers by
 //    direct global->LDS loads (next block in flight while the current one is
 //    consumed), S^T = K Q^T and dP^T = V dO^T (keys x queries),
 //    P^T = exp2(S^T * scale * log2e - LSE * log2e) with the causal mask,
@@ -35,14 +37,15 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ chunk_doc,
     const int32_t* __restrict__ doc_chunk_off, const int32_t* __restrict__ doc_kv_off,
     const int32_t* __restrict__ sel_clean, const int32_t* __restrict__ err, bf16* __restrict__ dq, int Hkv,
-    int C, int K, float scale, int T) {
+    int C, int K, int sub, float scale, int T) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;
   constexpr int NT = D / 32;
   constexpr int NW = kDqThreads / 64;
   __shared__ __attribute__((aligned(16))) KVTiles<D> buf0;
   __shared__ __attribute__((aligned(16))) KVTiles<D> buf1;
-  __shared__ int s_blocks[64];
+  __shared__ int s_blocks[64];   // kept 64-key tiles (a block of 128 keys is two)
+  __shared__ int s_slots[64];
   __shared__ int s_nblocks;
 
   if (err[1]) {
@@ -61,7 +64,8 @@ __global__ __launch_bounds__(kDqThreads, 2) void dq_kernel(
   const int Hq = Hkv * kQPerKV;
 
   if (threadIdx.x < 64) {
-    const int n = compact_selection(sel_clean + ((int64_t)i * C + g) * K, K, threadIdx.x, s_blocks, nullptr);
+    const int n = compact_tiles(sel_clean + ((int64_t)i * C + g) * K, K, sub, p0 + qcount - 1, threadIdx.x,
+                                s_blocks, s_slots);
     if (threadIdx.x == 0) s_nblocks = n;
   }
 
@@ -203,8 +207,8 @@ hipError_t launch_dq_recompute(const msa_problem& p, const void* q, const void* 
     hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kDqThreads), 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dout, lse, delta, cu,
                        sched + L.chunk_doc, sched + L.doc_chunk_off, sched + L.doc_kv_off, sched + L.sel_clean,
-                       sched + L.err, (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.softmax_scale,
-                       p.total_tokens);
+                       sched + L.err, (bf16*)dq, p.num_kv_heads, p.num_chunks, p.topk, p.block_size / kBlock,
+                       p.softmax_scale, p.total_tokens);
   };
   if (p.head_dim == 128) go(dq_kernel<128>);
   else go(dq_kernel<64>);

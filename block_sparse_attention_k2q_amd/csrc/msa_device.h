@@ -272,22 +272,6 @@ __device__ __forceinline__ void stage_block(bf16* tile, const bf16* __restrict__
   }
 }
 
-// Kept block ids of one cleaned selection row (K <= 64 slots, -1 = empty),
-// compacted in slot order into blocks[] (and their slot numbers into
-// slots[] when given).  Run by all 64 lanes of one wave; returns the count.
-__device__ __forceinline__ int compact_selection(const int32_t* __restrict__ row, int K, int lane,
-                                                 int* blocks, int* slots) {
-  const int b = lane < K ? row[lane] : -1;
-  const bool keep = b >= 0;
-  const uint64_t mask = __builtin_amdgcn_ballot_w64(keep);
-  const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-  if (keep) {
-    blocks[pos] = b;
-    if (slots) slots[pos] = lane;
-  }
-  return __popcll(mask);
-}
-
 // Kernel tiles hold kBlock = 64 keys; a selected block of `sub` * 64 keys
 // (key block 128: sub = 2) is taken as `sub` consecutive 64-key tiles.
 // Lane s < sub * K stands for tile `sub * row[s / sub] + s % sub` of slot

@@ -62,8 +62,8 @@ typedef struct msa_problem {
   int32_t num_kv_heads;    /* Hkv: index heads == KV heads (one index head per KV head) */
   int32_t q_per_kv;        /* query heads per KV head; must be 16 (8 queries x 16 heads = 128-row tile) */
   int32_t head_dim;        /* D: 64 or 128 */
-  int32_t block_size;      /* B: key block size, 64 or 128 (at 128: topk <= 32 and
-                              dq_mode MSA_DQ_DS_BUFFER) */
+  int32_t block_size;      /* B: key block size, 64 or 128 (at 128: topk <= 32; every
+                              dq_mode, each block taken as two 64-key tiles) */
   int32_t query_chunk;     /* must be 8 (msa_schedule: QUERY_CHUNK) */
   int32_t topk;            /* slots per (index head, chunk); 1..64 */
   int32_t num_chunks;      /* C = sum_d ceil(len_d / 8) */

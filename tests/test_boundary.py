@@ -72,8 +72,8 @@ def test_bad_problems_are_rejected_on_the_host(field, value, exc):
 
 
 def test_key_block_128_rules():
-    """Key block 128 runs as two 64-key tiles: topk <= 32, dQ from stored dS
-    only, and twice the dS slots of key block 64 at the same topk."""
+    """Key block 128 runs as two 64-key tiles: topk <= 32 in every dQ mode,
+    and twice the dS slots of key block 64 at the same topk."""
     p = B.Problem.make([0, 8192], 4, 128, 16, block_size=128, dq_mode=B.DQ_DS_BUFFER)
     assert p.num_kblocks == 64
     L = B.msa_schedule_layout_of(p)
@@ -81,10 +81,15 @@ def test_key_block_128_rules():
     base = 4 * 8192 * 64 + 2 * 4 * 8192 * 4 * 128
     slots = 4 * 1024 * 16 * 2
     assert base + slots * 128 * 64 * 2 <= B.msa_backward_scratch_bytes(p) < base + slots * 128 * 64 * 2 + 4096
-    for field, value in (("topk", 33), ("dq_mode", B.DQ_RECOMPUTE), ("dq_mode", B.DQ_ATOMIC_POOL),
-                         ("dq_mode", B.DQ_ATOMIC_POOL_BF16)):
+    for mode in (B.DQ_DS_BUFFER, B.DQ_RECOMPUTE, B.DQ_ATOMIC_POOL, B.DQ_ATOMIC_POOL_BF16):
+        q = B.Problem(**{**p.__dict__, "dq_mode": mode})
+        assert B.msa_schedule_layout_of(q).total == L.total
+        assert B.msa_backward_scratch_bytes(q) >= base
         with pytest.raises(NotImplementedError):
-            B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, field: value}))
+            B.msa_schedule_layout_of(B.Problem(**{**q.__dict__, "topk": 33}))
+    # without the dS slots the recompute mode needs only Delta and dK/dV
+    rq = B.Problem(**{**p.__dict__, "dq_mode": B.DQ_RECOMPUTE})
+    assert base <= B.msa_backward_scratch_bytes(rq) < base + 4096
     with pytest.raises(ValueError):   # 63 blocks of 128 cannot hold 8192 tokens
         B.msa_schedule_layout_of(B.Problem(**{**p.__dict__, "num_kblocks": 63}))
 

@@ -129,12 +129,16 @@ SMALL128 = {
 
 
 @pytest.mark.parametrize("case", list(SMALL128))
-@pytest.mark.parametrize("num_cus", [None, 7, 1])   # 1: the grid has no spare walk
-def test_small_cases_block128_full_parity(case, num_cus):
+@pytest.mark.parametrize("num_cus,dq_mode", [(None, B.DQ_DS_BUFFER), (7, B.DQ_DS_BUFFER),
+                                             (1, B.DQ_DS_BUFFER),   # 1: the grid has no spare walk
+                                             (None, B.DQ_RECOMPUTE), (7, B.DQ_RECOMPUTE),
+                                             (None, B.DQ_ATOMIC_POOL), (7, B.DQ_ATOMIC_POOL),
+                                             (None, B.DQ_ATOMIC_POOL_BF16), (1, B.DQ_ATOMIC_POOL_BF16)])
+def test_small_cases_block128_full_parity(case, num_cus, dq_mode):
     w = SMALL128[case]()
-    print(f"[case] {case} num_cus={num_cus} T={w.total_tokens} Hkv={w.num_kv_heads} "
+    print(f"[case] {case} num_cus={num_cus} dq_mode={dq_mode} T={w.total_tokens} Hkv={w.num_kv_heads} "
           f"D={w.head_dim} k={w.topk} block={w.block}", flush=True)
-    p = TL.problem_for(w, num_cus, B.DQ_DS_BUFFER)
+    p = TL.problem_for(w, num_cus, dq_mode)
     t = TL.to_dev(w)
     sched = TL.run_schedule(w, p, t)
     want = TL.compare_schedule(w, p, sched)
@@ -172,6 +176,8 @@ def _gpu_rows(x, toks, heads):
                          [(n, B.DQ_DS_BUFFER) for n in FULL] + [("single8k", B.DQ_ATOMIC_POOL),
                                                                 ("single8k", B.DQ_ATOMIC_POOL_BF16),
                                                                 ("single8k_b128", B.DQ_DS_BUFFER),
+                                                                ("single8k_b128", B.DQ_RECOMPUTE),
+                                                                ("single8k_b128", B.DQ_ATOMIC_POOL),
                                                                 ("varlen8_b128", B.DQ_DS_BUFFER),
                                                                 ("long64k_b128", B.DQ_DS_BUFFER)])
 def test_full_size_configs_sampled(name, dq_mode):

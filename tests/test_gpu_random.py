@@ -31,7 +31,7 @@ def _case(seed):
                       selection=str(rng.choice(["uniform", "zipf", "uniform_first"])), seed=2000 + seed)
     if rng.random() < 0.5:
         w = TL.inject_junk(w, 3000 + seed)
-    mode = B.DQ_DS_BUFFER if block == 128 else MODES[int(rng.integers(len(MODES)))]
+    mode = MODES[int(rng.integers(len(MODES)))]
     num_cus = [None, 7, 1, 3][int(rng.integers(4))]
     return w, mode, num_cus
 
