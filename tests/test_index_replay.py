@@ -78,6 +78,22 @@ def _replay(w, num_sms=256, kv_starts=None, kv_rows=None):
         # its byte offset in the scratch (16 KiB per slot) is formed in 64 bits
         assert (slot_idx.max(initial=0) + 1) * 16384 <= cap * sub * 16384
 
+    # --- atomic-pool backward: every tile of every task, live or not ---------
+    # (a tile after the chunk's last query computes zeros; its K / V rows are
+    # read only below the document end, and it flushes only when it starts
+    # inside the document, each key past the end going to the tile's first key)
+    for t in range(sub):
+        tile = sub * b + t
+        flushes = tile * 64 < ln
+        key = tile[:, None] * 64 + np.arange(64)[None, :]
+        kpos = np.where(key < ln[:, None], key, tile[:, None] * 64)
+        frow = kv0[:, None] + kpos
+        assert np.all(frow[flushes] >= 0) and frow[flushes].max(initial=0) < W
+        loaded = key < ln[:, None]
+        assert (kv0[:, None] + key)[loaded].max(initial=0) < W
+    # dQ pool rows: the chunk's tokens, rows past the document end sent to the tile's first row
+    assert ((tok0 + qb + qc - 1) * Hq + 16 * i + 15).max() < T * Hq
+
     # --- query-parallel forward and dQ kernels, per (index head, chunk) -----
     sc = s["sel_clean"].astype(np.int64)                # [Hkv, C, K]
     g = np.arange(lay.C)
