@@ -276,8 +276,11 @@ int msa_index_scratch_bytes(const msa_problem* p, size_t* bytes);
 int msa_index_select(const msa_problem* p, const void* qi, const void* ki, const int32_t* cu_seqlens,
                      void* scratch, int32_t* sel, void* stream);
 
-/* Grid size the main backward kernel is launched with (msa_schedule:
- * grid_launch_bound(capacity, num_cus), capacity = Hkv * C * topk). */
+/* Number of walks the main backward kernels are sized for (msa_schedule:
+ * grid_launch_bound(capacity, num_cus), capacity = Hkv * C * topk); they
+ * launch one workgroup per walk, or one per walk and query half (KV-parallel
+ * kernel) or per walk and 64-key half (atomic-pool kernel at key block 128);
+ * workgroups past desc's grid_walks return at once. */
 int64_t msa_grid_launch_bound(int64_t capacity, int32_t num_cus);
 
 const char* msa_status_string(int status);
