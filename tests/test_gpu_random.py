@@ -1,8 +1,8 @@
 """Randomised small problems (fixed seeds), compared element by element with
 the fp64 oracle: document lengths from 0 to 1500 tokens (empty, ragged,
 partial chunks and blocks), 1 to 4 index heads, head dim 64 or 128, top-k
-1..12, key block 64 or 128, the three selection generators, every dQ mode
-the block size allows, several compute-unit counts (walk regimes and tail
+1..12, key block 64 or 128, the three selection generators, every dQ mode,
+several compute-unit counts (walk regimes and tail
 walks), junk selection slots.  Small top-k leaves rows that attend to a few
 keys, whose outputs reach |out| > 4 (the bf16 bar of out_tolerance)."""
 import numpy as np
