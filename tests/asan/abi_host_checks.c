@@ -62,8 +62,9 @@ int main(void) {
   msa_problem b = p; b.head_dim = 96;   EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_UNSUPPORTED);
   b = p; b.q_per_kv = 8;                EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_UNSUPPORTED);
   b = p; b.topk = 65;                   EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_UNSUPPORTED);
-  b = p; b.block_size = 128; b.dq_mode = MSA_DQ_RECOMPUTE;
-  EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_UNSUPPORTED);
+  b = p; b.block_size = 128; b.num_kblocks = 64; b.dq_mode = MSA_DQ_RECOMPUTE;
+  EXPECT(msa_schedule_layout_of(&b, &L) == MSA_OK);   /* key block 128: every dQ mode */
+  b.topk = 33;                          EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_UNSUPPORTED);
   b = p; b.num_kblocks = 63;            EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_SHAPE);
   b = p; b.kv_rows = 8191;              EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_SHAPE);
   b = p; b.kv_rows = -1;                EXPECT(msa_schedule_layout_of(&b, &L) == MSA_ERR_INVALID);
