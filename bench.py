@@ -297,6 +297,7 @@ def main() -> int:
     main_dq_tflops = n_pairs * bwd_f / (main_dq_ms * 1e-3) / 1e12 if main_dq_ms > 0 else 0.0
     dominant_tflops = n_pairs * useful[dominant] / (dominant_ms * 1e-3) / 1e12 if dominant_ms > 0 else 0.0
 
+    traffic = measured_traffic(dominant, names_key)
     result = {
         "metric": "MSA fwd+bwd useful TFLOP/s and % of bf16 MFMA peak, 1xMI355X",
         "value": round(value, 3),
@@ -337,10 +338,16 @@ def main() -> int:
         "backward_pct_peak": round(100.0 * bwd_tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(dominant_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dominant_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(dominant, names_key),
+                     "traffic": traffic,
                      "kernel": KERNEL_NAMES[names_key][dominant],
                      "launch_ms": round(dominant_ms, 4)},
     }
+    if traffic is not None:
+        # the measured HBM bytes of one launch over its duration: how close the
+        # kernel's gathers run to the memory side's peak
+        traffic_gbps = traffic / (dominant_ms * 1e-3) / 1e9
+        result["roofline"]["traffic_GBps"] = round(traffic_gbps, 1)
+        result["roofline"]["traffic_frac_hbm_peak"] = round(traffic_gbps / PEAK_HBM_GBS, 4)
     # The index scorer (the step that produces the selection; not part of the
     # timed step): same workload, synthetic index projections.
     from block_sparse_attention_k2q_amd.workloads import make_index_inputs

@@ -29,6 +29,9 @@ def test_bench_json_line():
     assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and 0 < roof["frac"] < 1
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert roof["launch_ms"] > 0 and roof["kernel"].startswith("backward_kv_kernel")
+    if roof["traffic"] is not None:   # the committed counter summary matches this kernel's source
+        gbps = roof["traffic"] / (roof["launch_ms"] * 1e-3) / 1e9
+        assert abs(roof["traffic_GBps"] - gbps) < 1.0 and 0 < roof["traffic_frac_hbm_peak"] < 1.5
     assert d["config"]["selected_pairs"] == 61696
 
 
