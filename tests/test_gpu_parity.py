@@ -178,6 +178,9 @@ def _gpu_rows(x, toks, heads):
                                                                 ("single8k_b128", B.DQ_DS_BUFFER),
                                                                 ("single8k_b128", B.DQ_RECOMPUTE),
                                                                 ("single8k_b128", B.DQ_ATOMIC_POOL),
+                                                                ("varlen8_b128", B.DQ_RECOMPUTE),
+                                                                ("zipf16k_b128", B.DQ_ATOMIC_POOL_BF16),
+                                                                ("long64k_b128", B.DQ_RECOMPUTE),
                                                                 ("varlen8_b128", B.DQ_DS_BUFFER),
                                                                 ("long64k_b128", B.DQ_DS_BUFFER)])
 def test_full_size_configs_sampled(name, dq_mode):
