@@ -97,34 +97,74 @@ def measured_traffic(kernel: str, mode: str):
     return float(val.group(1))
 
 
-def cpu_baseline(w, sched_host, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle on the host cores, on a bounded sample of the same
-    workload (an even spread of (index head, chunk) pairs, forward +
-    backward of each), reported in useful TFLOP/s."""
+def _oracle_share(job):
+    """One worker's share of the CPU baseline, in a fresh process with one
+    BLAS thread: the fp64 oracle (forward + backward) on the given
+    (index head, chunk) pairs; returns its own wall time."""
+    paths, cu, sel_clean, block, scale, chunks = job
     import numpy as np
-    from oracle import msa_oracle as O
-    # the host cores this process may run on; the BLAS pool is pinned to that count
-    cores = len(os.sched_getaffinity(0))
     from threadpoolctl import threadpool_limits
-    limiter = threadpool_limits(limits=cores)
+    from oracle import msa_oracle as O
+    q, k, v, do = (np.load(path, mmap_mode="r") for path in paths)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.backward_gathered(q, k, v, do, cu, sel_clean, block, scale, chunks=chunks)
+        return time.perf_counter() - t0
+
+
+def _noop(x):
+    return x
+
+
+def cpu_baseline(w, sched_host, max_pairs: int = 8192) -> dict:
+    """The fp64 oracle on the host cores: the workload's (index head, chunk)
+    pairs (all of them, or an even spread of max_pairs), forward + backward
+    of each, sharded over one worker process per core (one BLAS thread
+    each), reported in useful TFLOP/s over the wall time of the sharded run.
+    The workers read fp32 copies of q, k, v, dO (the bf16 values, exact)
+    from memory-mapped files; every oracle call widens them to fp64 itself."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    import numpy as np
+    cores = len(os.sched_getaffinity(0))
     lay = sched_host["layout"]
     sel_clean = sched_host["sel_clean"]
-    order = [(i, g) for g in np.linspace(0, lay.C - 1, 256).astype(int) for i in range(w.num_kv_heads)]
+    pairs_all = [(i, g) for g in range(lay.C) for i in range(w.num_kv_heads) if (sel_clean[i, g] >= 0).any()]
+    if len(pairs_all) > max_pairs:
+        pick = np.linspace(0, len(pairs_all) - 1, max_pairs).astype(int)
+        pairs_all = [pairs_all[x] for x in pick]
+    # each worker holds fp64 q, dO and the dq, out it writes: 32 bytes per element of q
+    per_worker = 32 * w.q.numel()
+    workers = max(1, min(cores, len(pairs_all), int((96 << 30) // per_worker)))
+    shares = [pairs_all[x::workers] for x in range(workers)]
+    tmp = tempfile.mkdtemp(prefix="msa_baseline_")
+    try:
+        paths = []
+        for name, t in (("q", w.q), ("k", w.k), ("v", w.v), ("do", w.do)):
+            path = os.path.join(tmp, name + ".npy")
+            np.save(path, t.float().numpy())
+            paths.append(path)
+        jobs = [(paths, w.cu_seqlens, sel_clean, w.block, w.scale, share) for share in shares]
+        # fresh interpreters (no GPU state inherited); a worker that dies
+        # fails the run instead of being restarted
+        with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as pool:
+            list(pool.map(_noop, range(workers)))      # workers started and imported
+            t0 = time.perf_counter()
+            list(pool.map(_oracle_share, jobs))
+            dt = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    blocks = int(sum((sel_clean[i, g] >= 0).sum() for i, g in pairs_all))
     fwd_f, bwd_f = pair_flops(w.block, w.head_dim)
-    done, pairs, t0 = [], 0, time.perf_counter()
-    for i, g in order:
-        O.backward_gathered(w.q, w.k, w.v, w.do, w.cu_seqlens, sel_clean, w.block, w.scale,
-                            chunks=[(i, int(g))])
-        pairs += int((sel_clean[i, g] >= 0).sum())
-        done.append((i, g))
-        if time.perf_counter() - t0 > budget_s and len(done) >= 8:
-            break
-    dt = time.perf_counter() - t0
-    limiter.unregister()
-    return {"value": pairs * (fwd_f + bwd_f) / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    n_all = int(sum((sel_clean[i, g] >= 0).any() for g in range(lay.C) for i in range(w.num_kv_heads)))
+    what = "all" if len(pairs_all) == n_all else f"an even spread of {len(pairs_all)} of the {n_all}"
+    return {"value": blocks * (fwd_f + bwd_f) / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"{len(done)} (index head, chunk) pairs of the {WORKLOAD} workload spread evenly "
-                      f"over chunks, {pairs} selected blocks, fp64 forward+backward, {dt:.1f} s"}
+            "sample": f"{what} (index head, chunk) pairs of the {WORKLOAD} workload ({blocks} selected "
+                      f"blocks), fp64 forward+backward, sharded over {workers} worker processes with one "
+                      f"BLAS thread each, {dt:.1f} s wall"}
 
 
 def main() -> int:

@@ -40,3 +40,18 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=60, cwd=ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_shards_the_oracle_over_worker_processes():
+    # the oracle's leg of the bench on the tiny workload, on the CPU: every
+    # (index head, chunk) pair of it, one worker process per usable core
+    import bench
+    from block_sparse_attention_k2q_amd.workloads import make_workload
+    from oracle import msa_oracle as O
+    w = make_workload("tiny")
+    s = O.build_schedule(w.sel, w.cu_seqlens, w.block, 256)
+    r = bench.cpu_baseline(w, s)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= len(os.sched_getaffinity(0))
+    blocks = int((s["sel_clean"] >= 0).sum())
+    assert r["sample"].startswith("all ") and f"({blocks} selected blocks)" in r["sample"]
