@@ -66,6 +66,8 @@ TASK_COLUMNS = ("index_head", "row_linear", "q_begin", "q_count",
 
 def f64(x) -> np.ndarray:
     """Widen a bf16/fp32 torch tensor or array to fp64 numpy (exact)."""
+    if isinstance(x, np.ndarray):   # numpy input: no torch import needed
+        return np.asarray(x, dtype=np.float64)
     try:
         import torch
         if isinstance(x, torch.Tensor):
